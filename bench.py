@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the microscaling hot path on one MI355X.
+
+One step = one W4A4 linear layer at Llama-8B MLP shape, on synthetic data:
+  quantize A (bf16 8192 x 4096 ~ N(0, 1))      -> MXFP4 codes + E8M0 scales + stats
+  quantize B (bf16 14336 x 4096 ~ N(0, .02^2)) -> MXFP4 codes + E8M0 scales + stats
+  C = deq(A) . deq(B)^T on the block-scaled FP4 MFMA, fp32 accumulate, bf16 out
+(MXFP4 = 1x32 E2M1 blocks with E8M0 scales, floor rule, round-to-nearest-even).
+
+Reported: quantizer GB/s (algorithmic bytes: 2 B read + 0.5 B codes + 1/32 B
+scale per element) as `value`, GEMM TFLOP/s (2 M N K per product), each with
+its fraction of the MI355X peak, QSNR of A, B (eq. (1)) and of the product
+(eq. (2)) against the bf16 product, and the CPU oracle timed on this host.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+M, N, K = 8192, 14336, 4096
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
+QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 32
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=3, help="input sets rotated to defeat the 256 MB MALL")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the quantizer and the GEMM shard "
+                          "without communication (see DESIGN.md), and no multi-GPU figure is produced",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import microscaling_block_quantization_amd as mx
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a_np, b_np = synth.w5(M, N, K)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    A = [up(a_np)]
+    B = [up(b_np)]
+    for _ in range(args.sets - 1):
+        A.append(A[0].clone())
+        B.append(B[0].clone())
+    fmt = mx.MXFP4
+    qa = mx.alloc_qtensor(fmt, M, K, dev)
+    qb = mx.alloc_qtensor(fmt, N, K, dev)
+    wsa = mx.alloc_workspace(fmt, M, K, dev)
+    wsb = mx.alloc_workspace(fmt, N, K, dev)
+    sta = torch.empty(64, dtype=torch.uint8, device=dev)
+    stb = torch.empty(64, dtype=torch.uint8, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nev = 4
+    def step(i, ev=None):
+        s = i % args.sets
+        if ev: ev[0].record()
+        mx.mx_quantize(fmt, A[s], out=qa, stats=sta, workspace=wsa)
+        if ev: ev[1].record()
+        mx.mx_quantize(fmt, B[s], out=qb, stats=stb, workspace=wsb)
+        if ev: ev[2].record()
+        mx.mx_gemm(fmt, qa, fmt, qb, c=C)
+        if ev: ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    qa_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    qb_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    g_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+
+    quant_bytes = (M + N) * K * QUANT_BYTES_PER_ELEM
+    quant_gbs = quant_bytes / ((qa_ms + qb_ms) * 1e-3) / 1e9
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+
+    # fidelity: eq. (1) for A and B from the fused statistics, eq. (2) for the product
+    st_a, st_b = mx.stats_to_dict(sta), mx.stats_to_dict(stb)
+    qsnr = lambda st: 10 * np.log10(st["sig2"] / st["err2"])
+    R = torch.matmul(A[0], B[0].t().contiguous()).float()     # bf16 reference product (hipBLASLt)
+    _, qsnr_ab = mx.mx_qsnr(R, C.float())
+    del R
+
+    out = {
+        "metric": "quantize GB/s (% HBM peak) + MXFP4 GEMM TFLOP/s (% MFMA peak) on 1 MI355X",
+        "value": round(quant_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->e2m1",
+        "data": "synthetic",
+        "config": {"workload": "W4A4 linear layer: MXFP4-quantize A bf16 8192x4096 N(0,1) and "
+                               "B bf16 14336x4096 N(0,0.02^2) (1x32 E2M1, E8M0 floor, RTNE, fused stats), "
+                               "then C = A.B^T on block-scaled FP4 MFMA, bf16 out",
+                   "M": M, "N": N, "K": K, "quant_bytes_per_step": quant_bytes},
+        "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
+                     "ms_a": round(qa_ms, 4), "ms_b": round(qb_ms, 4)},
+        "gemm": {"tflops": round(gemm_tflops, 1), "frac_fp4_peak": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+                 "ms": round(g_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "block-scaled MXFP4 GEMM",
+                     "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None},
+        "quantize_roofline": {"bound": "hbm", "kernel": "MXFP4 row quantizer (+ stats finalize)",
+                              "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "qsnr_db": {"A": round(qsnr(st_a), 4), "B": round(qsnr(st_b), 4), "AB": round(qsnr_ab, 4)},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        t0 = time.perf_counter()
+        ra = oracle.quantize(a_np, oracle.Format())
+        rb = oracle.quantize(b_np, oracle.Format())
+        tq = time.perf_counter() - t0
+        rows = 256
+        t0 = time.perf_counter()
+        oracle.gemm_f64(ra["dequant"][:rows], rb["dequant"])
+        tg = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(quant_bytes / tq / 1e9, 4), "unit": "GB/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"full quantize of A and B ({(M + N) * K} elements, {tq:.2f} s); "
+                      f"GEMM sample {rows}x{N}x{K} float64 in {tg:.2f} s",
+            "gemm_tflops": round(2.0 * rows * N * K / tg / 1e12, 5),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

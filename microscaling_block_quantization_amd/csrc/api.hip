@@ -1,0 +1,297 @@
+// api.hip -- the extern "C" entry points of libmx.so (declared in include/mx.h):
+// argument validation, buffer-size queries and kernel dispatch.  Every check
+// happens before the first launch; the library allocates nothing.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mx.h"
+#include "mx_kernels.hpp"
+
+using mxk::QParams;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t round_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Validate a format for a rows x cols tensor.  Returns MX_OK or an error code.
+int check_format(const mx_format* f, int64_t rows, int64_t cols) {
+    if (!f) return MX_ERR_ARG;
+    if (f->elem < 0 || f->elem > MX_ELEM_E3M0) return MX_ERR_ARG;
+    if (f->scale < 0 || f->scale > MX_SCALE_E3M0) return MX_ERR_ARG;
+    if (f->rule < 0 || f->rule > MX_RULE_OAS) return MX_ERR_ARG;
+    if (f->round < 0 || f->round > MX_ROUND_CEIL) return MX_ERR_ARG;
+    if (f->asymmetric != 0 && f->asymmetric != 1) return MX_ERR_ARG;
+    if (rows < 0 || cols < 0) return MX_ERR_ARG;
+    const int br = f->block_rows, bc = f->block_cols;
+    if (br < 1 || bc < 1 || !is_pow2(br) || !is_pow2(bc)) return MX_ERR_ARG;
+    if (rows % br || cols % bc) return MX_ERR_ARG;
+    if (br == 1) {
+        if (bc < 8 || bc > 256) return MX_ERR_UNSUPPORTED;
+    } else {
+        if (br < 8 || br > 32) return MX_ERR_UNSUPPORTED;
+        if (bc != 1 && bc != br) return MX_ERR_UNSUPPORTED;
+    }
+    if (cols % 8) return MX_ERR_UNSUPPORTED;
+    const mxd::Elem E = mxd::make_elem(f->elem, f->asymmetric);
+    if (f->asymmetric) {
+        if (f->elem != MX_ELEM_E2M1 && f->elem != MX_ELEM_INT4) return MX_ERR_UNSUPPORTED;
+        if (f->scale != MX_SCALE_E8M0 || f->hadamard || f->macro_cols) return MX_ERR_UNSUPPORTED;
+    }
+    if (f->rule == MX_RULE_OAS && (f->scale == MX_SCALE_E8M0 || f->macro_cols)) {
+        if (!(f->oas_tau >= E.qmax && f->oas_tau < 2.0f * E.qmax)) return MX_ERR_ARG;
+    }
+    if (f->hadamard) {
+        const int h = f->hadamard;
+        if (h != 16 && h != 32 && h != 64 && h != 128) return MX_ERR_UNSUPPORTED;
+        if (br != 1 || cols % h) return MX_ERR_UNSUPPORTED;
+    }
+    if (f->macro_cols) {
+        if (f->macro_cols != 128) return MX_ERR_ARG;
+        if (br != 1 || 128 % bc || cols % 128 || f->scale != MX_SCALE_E8M0) return MX_ERR_UNSUPPORTED;
+    }
+    return MX_OK;
+}
+
+int64_t crow_bytes(const mx_format* f, int64_t cols) {
+    return (f->elem == MX_ELEM_FP6_E2M3 || f->elem == MX_ELEM_FP6_E3M2) ? cols * 3 / 4 : cols / 2;
+}
+
+QParams make_params(const mx_format* f, int in_bf16, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                    const mx_qtensor* q) {
+    QParams p;
+    memset(&p, 0, sizeof(p));
+    p.x = x;
+    p.rows = rows;
+    p.cols = cols;
+    p.ld = ld;
+    p.in_bf16 = in_bf16;
+    p.codes = static_cast<uint8_t*>(q->codes);
+    p.scales = static_cast<uint8_t*>(q->scales);
+    p.offsets = static_cast<uint16_t*>(q->offsets);
+    p.macro = static_cast<uint8_t*>(q->macro_scales);
+    p.tensor_scale = q->tensor_scale;
+    p.ref_exp = q->ref_exp;
+    p.elem = f->elem;
+    p.asym = f->asymmetric;
+    p.scale = f->scale;
+    p.rule = f->rule;
+    p.round = f->round;
+    p.br = f->block_rows;
+    p.bc = f->block_cols;
+    p.had = f->hadamard;
+    p.macro_cols = f->macro_cols;
+    p.tau = f->oas_tau;
+    p.seed = f->seed;
+    p.off = f->rng_offset;
+    return p;
+}
+
+bool needs_prepass(const mx_format* f) { return f->scale == MX_SCALE_NVFP4 || f->scale == MX_SCALE_E3M0; }
+
+int64_t quant_grid(const QParams& p) {
+    if (p.br > 1) return mxk::tiles_grid(p);
+    if (mxk::rows_fast_ok(p)) return mxk::rows_fast_grid(p);
+    return mxk::rows_grid(p);
+}
+
+struct Workspace {
+    size_t stats_off, stats_bytes, amax_off, amax_bytes, total;
+};
+
+Workspace workspace_layout(const mx_format* f, int in_bf16, int64_t rows, int64_t cols) {
+    mx_qtensor dummy;
+    memset(&dummy, 0, sizeof(dummy));
+    QParams p = make_params(f, in_bf16, nullptr, rows, cols, cols, &dummy);
+    Workspace w;
+    // sized for the larger of the two input dtypes' grids so one query fits both
+    p.in_bf16 = 0;
+    int64_t g0 = quant_grid(p);
+    p.in_bf16 = 1;
+    int64_t g1 = quant_grid(p);
+    int64_t g = g0 > g1 ? g0 : g1;
+    (void)in_bf16;
+    w.stats_off = 0;
+    w.stats_bytes = round_up((size_t)g * sizeof(mxd::StatPart));
+    w.amax_off = w.stats_bytes;
+    w.amax_bytes = needs_prepass(f) ? round_up((size_t)mxk::amax_grid(p) * sizeof(float)) : 0;
+    w.total = w.stats_bytes + w.amax_bytes;
+    return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(int status) {
+    switch (status) {
+    case MX_OK: return "ok";
+    case MX_ERR_ARG: return "invalid argument";
+    case MX_ERR_UNSUPPORTED: return "format or shape not supported by this build";
+    case MX_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case MX_ERR_WORKSPACE: return "workspace missing or too small";
+    case MX_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int mx_query_sizes(const mx_format* f, int64_t rows, int64_t cols, mx_sizes* out) {
+    int rc = check_format(f, rows, cols);
+    if (rc) return rc;
+    if (!out) return MX_ERR_ARG;
+    const int64_t nblk = (rows / f->block_rows) * (cols / f->block_cols);
+    out->codes = (size_t)(rows * crow_bytes(f, cols));
+    out->scales = (size_t)nblk;
+    out->offsets = f->asymmetric ? (size_t)nblk * 2 : 0;
+    out->macro_scales = f->macro_cols ? (size_t)(rows * (cols / 128)) : 0;
+    out->tensor_scale = f->scale == MX_SCALE_NVFP4 ? sizeof(float) : 0;
+    out->ref_exp = f->scale == MX_SCALE_E3M0 ? sizeof(int32_t) : 0;
+    out->workspace = workspace_layout(f, 1, rows, cols).total;
+    return MX_OK;
+}
+
+int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                const mx_qtensor* out, void* dequant, int dq_dtype, mx_stats* stats, void* workspace,
+                size_t ws_bytes, void* stream) {
+    int rc = check_format(f, rows, cols);
+    if (rc) return rc;
+    if (in_dtype != MX_DTYPE_F32 && in_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+    if (dequant && dq_dtype != MX_DTYPE_F32 && dq_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+    if (!out || ld < cols) return MX_ERR_ARG;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!x || !out->codes || !out->scales)) return MX_ERR_ARG;
+    if (f->asymmetric && n > 0 && !out->offsets) return MX_ERR_ARG;
+    if (f->macro_cols && n > 0 && !out->macro_scales) return MX_ERR_ARG;
+    if (f->scale == MX_SCALE_NVFP4 && !out->tensor_scale) return MX_ERR_ARG;
+    if (f->scale == MX_SCALE_E3M0 && !out->ref_exp) return MX_ERR_ARG;
+    const int esz = in_dtype == MX_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(x) || !aligned16(out->codes) || !aligned16(dequant) || ((ld * esz) & 15)) return MX_ERR_ALIGN;
+    if (!aligned16(out->offsets) || !aligned16(stats)) return MX_ERR_ALIGN;
+    const Workspace W = workspace_layout(f, in_dtype == MX_DTYPE_BF16, rows, cols);
+    const bool need_ws = stats || needs_prepass(f);
+    if (need_ws && (!workspace || ws_bytes < W.total)) return MX_ERR_WORKSPACE;
+    if (need_ws && !aligned16(workspace)) return MX_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    QParams p = make_params(f, in_dtype == MX_DTYPE_BF16, x, rows, cols, ld, out);
+    p.dq = dequant;
+    p.dq_bf16 = dq_dtype == MX_DTYPE_BF16;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+    if (needs_prepass(f)) {
+        QParams a = p;
+        a.amax_parts = reinterpret_cast<float*>(ws + W.amax_off);
+        const int64_t ga = n > 0 ? mxk::amax_grid(a) : 0;
+        if (ga > 0) {
+            rc = hip_status(mxk::launch_amax(a, s));
+            if (rc) return rc;
+        }
+        const mxd::Elem E = mxd::make_elem(f->elem, f->asymmetric);
+        rc = hip_status(mxk::launch_tensor_scale(a.amax_parts, ga, f->scale, E.qmax, out->tensor_scale,
+                                                 out->ref_exp, s));
+        if (rc) return rc;
+    }
+    int64_t grid = n > 0 ? quant_grid(p) : 0;
+    if (stats) p.parts = reinterpret_cast<mxd::StatPart*>(ws + W.stats_off);
+    if (grid > 0) {
+        hipError_t e;
+        if (p.br > 1) e = mxk::launch_tiles(p, s);
+        else if (mxk::rows_fast_ok(p)) e = mxk::launch_rows_fast(p, s);
+        else e = mxk::launch_rows(p, false, s);
+        rc = hip_status(e);
+        if (rc) return rc;
+    }
+    if (stats) {
+        rc = hip_status(mxk::launch_stats_final(p.parts, grid, n, stats, s));
+        if (rc) return rc;
+    }
+    return MX_OK;
+}
+
+int mx_dequantize(const mx_format* f, const mx_qtensor* q, int out_dtype, void* y, int64_t ld, void* stream) {
+    if (!q) return MX_ERR_ARG;
+    int rc = check_format(f, q->rows, q->cols);
+    if (rc) return rc;
+    if (out_dtype != MX_DTYPE_F32 && out_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+    if (ld < q->cols) return MX_ERR_ARG;
+    const int64_t n = q->rows * q->cols;
+    if (n == 0) return MX_OK;
+    if (!y || !q->codes || !q->scales) return MX_ERR_ARG;
+    if (f->asymmetric && !q->offsets) return MX_ERR_ARG;
+    if (f->macro_cols && !q->macro_scales) return MX_ERR_ARG;
+    if (f->scale == MX_SCALE_NVFP4 && !q->tensor_scale) return MX_ERR_ARG;
+    if (f->scale == MX_SCALE_E3M0 && !q->ref_exp) return MX_ERR_ARG;
+    const int esz = out_dtype == MX_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(y) || !aligned16(q->codes) || ((ld * esz) & 15)) return MX_ERR_ALIGN;
+    QParams p = make_params(f, 0, nullptr, q->rows, q->cols, ld, q);
+    p.dq = y;
+    p.dq_bf16 = out_dtype == MX_DTYPE_BF16;
+    return hip_status(mxk::launch_dequant(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t mx_qsnr_workspace_size(int64_t n) {
+    if (n < 0) return 0;
+    return round_up((size_t)mxk::qsnr_grid(n) * sizeof(mxd::StatPart)) + round_up(sizeof(mx_stats));
+}
+
+int mx_qsnr(int dtype, const void* ref, const void* approx, int64_t n, mx_stats* host_stats, double* qsnr_db,
+            void* workspace, size_t ws_bytes, void* stream) {
+    if (dtype != MX_DTYPE_F32 && dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+    if (n <= 0 || !ref || !approx || !qsnr_db) return MX_ERR_ARG;
+    if (!aligned16(ref) || !aligned16(approx)) return MX_ERR_ALIGN;
+    const size_t need = mx_qsnr_workspace_size(n);
+    if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MX_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    mxd::StatPart* parts = reinterpret_cast<mxd::StatPart*>(ws);
+    void* fin = ws + round_up((size_t)mxk::qsnr_grid(n) * sizeof(mxd::StatPart));
+    int rc = hip_status(mxk::launch_qsnr(dtype == MX_DTYPE_BF16, ref, approx, n, parts, s));
+    if (rc) return rc;
+    rc = hip_status(mxk::launch_stats_final(parts, mxk::qsnr_grid(n), n, fin, s));
+    if (rc) return rc;
+    mx_stats st;
+    if (hipMemcpyAsync(&st, fin, sizeof(st), hipMemcpyDeviceToHost, s) != hipSuccess) return MX_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MX_ERR_HIP;
+    if (host_stats) *host_stats = st;
+    if (!(st.sig2 > 0)) return MX_ERR_ARG;
+    *qsnr_db = st.err2 > 0 ? 10.0 * log10(st.sig2 / st.err2) : INFINITY;
+    return MX_OK;
+}
+
+int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const mx_qtensor* b, void* c,
+            int64_t ldc, int c_dtype, void* stream) {
+    if (!fa || !fb || !a || !b) return MX_ERR_ARG;
+    for (const mx_format* f : {fa, fb}) {
+        if (f->elem != MX_ELEM_E2M1 || f->scale != MX_SCALE_E8M0 || f->block_rows != 1 ||
+            f->block_cols != 32 || f->asymmetric || f->hadamard || f->macro_cols)
+            return MX_ERR_UNSUPPORTED;
+    }
+    int rc = check_format(fa, a->rows, a->cols);
+    if (rc) return rc;
+    rc = check_format(fb, b->rows, b->cols);
+    if (rc) return rc;
+    const int64_t M = a->rows, N = b->rows, K = a->cols;
+    if (b->cols != K) return MX_ERR_ARG;
+    if (c_dtype != MX_DTYPE_F32 && c_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+    if (K % 128) return MX_ERR_UNSUPPORTED;
+    if (ldc < N) return MX_ERR_ARG;
+    if (M == 0 || N == 0) return MX_OK;
+    if (K == 0) return MX_ERR_UNSUPPORTED;
+    if (!c || !a->codes || !a->scales || !b->codes || !b->scales) return MX_ERR_ARG;
+    if (!aligned16(c) || !aligned16(a->codes) || !aligned16(b->codes) || !aligned16(a->scales) ||
+        !aligned16(b->scales))
+        return MX_ERR_ALIGN;
+    return hip_status(mxk::launch_gemm(static_cast<const uint8_t*>(a->codes), static_cast<const uint8_t*>(a->scales),
+                                       static_cast<const uint8_t*>(b->codes), static_cast<const uint8_t*>(b->scales),
+                                       c, M, N, K, ldc, c_dtype == MX_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// mx_kernels.hpp -- launch interface between the C ABI (api.hip) and the
+// kernel translation units.  Internal to libmx.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_device.hpp"
+
+namespace mxk {
+
+// Everything a quantization launch needs.  Device pointers except where noted.
+struct QParams {
+    const void* x;
+    int64_t rows, cols, ld;        // ld in elements
+    int in_bf16;
+    uint8_t* codes;
+    uint8_t* scales;
+    uint16_t* offsets;
+    uint8_t* macro;
+    const float* tensor_scale;     // NVFP4 g, produced by the pre-pass
+    const int32_t* ref_exp;        // E3M0 e_ref, produced by the pre-pass
+    void* dq;                      // nullable
+    int dq_bf16;
+    mxd::StatPart* parts;          // nullable: one partial per workgroup
+    float* amax_parts;             // pre-pass mode: one max per workgroup
+    int elem, asym, scale, rule, round;
+    int br, bc, had, macro_cols;
+    float tau;
+    uint64_t seed, off;
+};
+
+constexpr int NT = 256;   // threads per workgroup for the streaming kernels
+
+// row blocks (block_rows == 1): generic kernel; returns number of workgroups
+int64_t rows_grid(const QParams& p);
+hipError_t launch_rows(const QParams& p, bool amax_only, hipStream_t s);
+// the E2M1 / E8M0 / RTNE row path on the hardware FP4 converter
+bool rows_fast_ok(const QParams& p);
+int64_t rows_fast_grid(const QParams& p);
+hipError_t launch_rows_fast(const QParams& p, hipStream_t s);
+// column (b x 1) and 2D (b x b) blocks
+int64_t tiles_grid(const QParams& p);
+hipError_t launch_tiles(const QParams& p, hipStream_t s);
+// plain tensor abs-max pre-pass (no rotation)
+int64_t amax_grid(const QParams& p);
+hipError_t launch_amax(const QParams& p, hipStream_t s);
+// finalize: tensor scale / reference exponent from the per-workgroup maxima
+hipError_t launch_tensor_scale(const float* parts, int64_t n, int scale_kind, float qmax,
+                               float* tensor_scale, int32_t* ref_exp, hipStream_t s);
+// finalize: statistics from per-workgroup partials, fixed order
+hipError_t launch_stats_final(const mxd::StatPart* parts, int64_t n, int64_t nelem, void* out,
+                              hipStream_t s);
+// dequantize
+hipError_t launch_dequant(const QParams& p, hipStream_t s);
+// QSNR partials between two tensors
+int64_t qsnr_grid(int64_t n);
+hipError_t launch_qsnr(int bf16, const void* a, const void* b, int64_t n, mxd::StatPart* parts,
+                       hipStream_t s);
+// MXFP4 GEMM
+hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                       void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16,
+                       hipStream_t s);
+
+}  // namespace mxk
