@@ -159,7 +159,8 @@ int mx_query_sizes(const mx_format *f, int64_t rows, int64_t cols, mx_sizes *out
  * dequant (nullable): the dequantized tensor, rows x cols dense, dtype dq_dtype
  * (fake quantization).  stats (nullable, device): the statistics of x against
  * its dequantized values, written when the stream reaches them.  workspace:
- * device scratch of at least mx_query_sizes().workspace bytes.
+ * device scratch of at least mx_query_sizes().workspace bytes (no initial
+ * contents needed); calls that share one workspace must not overlap.
  * Shapes this build runs: rows % block_rows == 0 and cols % block_cols == 0;
  * row blocks b in {8, 16, 32, 64, 128, 256} with cols % 8 == 0; column and 2D
  * blocks b in {8, 16, 32}; ld a multiple of 16 bytes.                       */

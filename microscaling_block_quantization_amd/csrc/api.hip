@@ -118,9 +118,9 @@ Workspace workspace_layout(const mx_format* f, int in_bf16, int64_t rows, int64_
     (void)in_bf16;
     w.stats_off = 0;
     w.stats_bytes = round_up((size_t)g * sizeof(mxd::StatPart));
-    w.amax_off = w.stats_bytes;
+    w.amax_off = w.stats_off + w.stats_bytes;
     w.amax_bytes = needs_prepass(f) ? round_up((size_t)mxk::amax_grid(p) * sizeof(float)) : 0;
-    w.total = w.stats_bytes + w.amax_bytes;
+    w.total = w.amax_off + w.amax_bytes;
     return w;
 }
 
@@ -203,7 +203,7 @@ int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, i
     if (grid > 0) {
         hipError_t e;
         if (p.br > 1) e = mxk::launch_tiles(p, s);
-        else if (mxk::rows_fast_ok(p)) e = mxk::launch_rows_fast(p, s);
+        else if (mxk::rows_fast_ok(p)) e = mxk::launch_rows_fast(p, s, &grid);
         else e = mxk::launch_rows(p, false, s);
         rc = hip_status(e);
         if (rc) return rc;

@@ -43,9 +43,21 @@ __global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64
     __shared__ unsigned long long su[3][NT];
     double s2 = 0, e2 = 0;
     unsigned long long nz = 0, fl = 0, zb = 0;
-    for (int64_t i = threadIdx.x; i < n; i += NT) {
-        StatPart p = parts[i];
-        s2 += p.sig2; e2 += p.err2; nz += p.nonzero; fl += p.flushed; zb += p.zero_blocks;
+    // each thread owns the partials t, t + NT, ...; eight of them are loaded
+    // before any is added so the loads overlap
+    constexpr int U = 8;
+    for (int64_t base = threadIdx.x; base < n; base += (int64_t)NT * U) {
+        StatPart q[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t i = base + (int64_t)u * NT;
+            if (i < n) q[u] = parts[i];
+            else q[u] = StatPart{0.0, 0.0, 0ull, 0ull, 0ull, 0ull};
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            s2 += q[u].sig2; e2 += q[u].err2; nz += q[u].nonzero; fl += q[u].flushed; zb += q[u].zero_blocks;
+        }
     }
     const int t = threadIdx.x;
     sd[0][t] = s2; sd[1][t] = e2; su[0][t] = nz; su[1][t] = fl; su[2][t] = zb;

@@ -307,10 +307,12 @@ __device__ __forceinline__ T wave_sum(T v) {
 }
 
 // block-wide sum of one StatPart per thread; thread 0 writes it to dst
+// Workgroup sums of the per-thread statistics, valid in thread 0.  Wave
+// butterflies then the waves in index order: the result does not depend on
+// timing.
 template <int NT>
-__device__ __forceinline__ void block_stats(double s2, double e2, unsigned long long nz,
-                                            unsigned long long fl, unsigned long long zb,
-                                            StatPart* dst) {
+__device__ __forceinline__ StatPart block_sum(double s2, double e2, unsigned long long nz,
+                                              unsigned long long fl, unsigned long long zb) {
     __shared__ double sh_d[2][NT / 64];
     __shared__ unsigned long long sh_u[3][NT / 64];
     s2 = wave_sum(s2);
@@ -324,15 +326,23 @@ __device__ __forceinline__ void block_stats(double s2, double e2, unsigned long 
         sh_u[0][w] = nz; sh_u[1][w] = fl; sh_u[2][w] = zb;
     }
     __syncthreads();
+    StatPart p;
+    p.sig2 = 0; p.err2 = 0; p.nonzero = 0; p.flushed = 0; p.zero_blocks = 0; p.pad = 0;
     if (threadIdx.x == 0) {
-        StatPart p;
-        p.sig2 = 0; p.err2 = 0; p.nonzero = 0; p.flushed = 0; p.zero_blocks = 0; p.pad = 0;
         for (int i = 0; i < NT / 64; i++) {
             p.sig2 += sh_d[0][i]; p.err2 += sh_d[1][i];
             p.nonzero += sh_u[0][i]; p.flushed += sh_u[1][i]; p.zero_blocks += sh_u[2][i];
         }
-        *dst = p;
     }
+    return p;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_stats(double s2, double e2, unsigned long long nz,
+                                            unsigned long long fl, unsigned long long zb,
+                                            StatPart* dst) {
+    const StatPart p = block_sum<NT>(s2, e2, nz, fl, zb);
+    if (threadIdx.x == 0) *dst = p;
 }
 
 }  // namespace mxd

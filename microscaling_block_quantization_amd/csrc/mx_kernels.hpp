@@ -36,8 +36,8 @@ int64_t rows_grid(const QParams& p);
 hipError_t launch_rows(const QParams& p, bool amax_only, hipStream_t s);
 // the E2M1 / E8M0 / RTNE row path on the hardware FP4 converter
 bool rows_fast_ok(const QParams& p);
-int64_t rows_fast_grid(const QParams& p);
-hipError_t launch_rows_fast(const QParams& p, hipStream_t s);
+int64_t rows_fast_grid(const QParams& p);   // upper bound of the grid launch_rows_fast uses
+hipError_t launch_rows_fast(const QParams& p, hipStream_t s, int64_t* grid);
 // column (b x 1) and 2D (b x b) blocks
 int64_t tiles_grid(const QParams& p);
 hipError_t launch_tiles(const QParams& p, hipStream_t s);
