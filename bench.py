@@ -15,6 +15,7 @@ its fraction of the MI355X peak, QSNR of A, B (eq. (1)) and of the product
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +25,26 @@ M, N, K = 8192, 14336, 4096
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
 QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 32
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def counted_traffic(key):
+    """HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters
+    (profiles/traffic.json), or None when the kernel's sources changed since."""
+    try:
+        with open(os.path.join(HERE, "profiles", "traffic.json")) as f:
+            k = json.load(f)["kernels"][key]
+        h = hashlib.sha256()
+        for src in k["sources"]:
+            with open(os.path.join(HERE, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != k["sha"]:
+            return None
+        return k
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -42,8 +63,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU; the quantizer and the GEMM shard "
-                          "without communication (see DESIGN.md), and no multi-GPU figure is produced",
+        print(json.dumps({"error": "one GPU only: the quantizer and the GEMM shard by rows without "
+                          "communication, and no multi-GPU figure is produced",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -112,6 +133,29 @@ def main():
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
 
+    # for information, outside the timed steps: the quantizer alone (codes and
+    # scales, no statistics), the form a layer uses when fidelity is not wanted
+    reps = 10
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(reps):
+        s = i % args.sets
+        ev2[i][0].record()
+        mx.mx_quantize(fmt, A[s], out=qa, workspace=wsa)
+        ev2[i][1].record()
+        mx.mx_quantize(fmt, B[s], out=qb, workspace=wsb)
+        ev2[i][2].record()
+    torch.cuda.synchronize()
+    qa0 = sum(e[0].elapsed_time(e[1]) for e in ev2) / reps
+    qb0 = sum(e[1].elapsed_time(e[2]) for e in ev2) / reps
+    quant0_gbs = quant_bytes / ((qa0 + qb0) * 1e-3) / 1e9
+    # the step left A's and B's codes of the last input set; recompute them (and
+    # the product) for the fidelity figures below
+    s_last = (args.steps - 1) % args.sets
+    mx.mx_quantize(fmt, A[s_last], out=qa, stats=sta, workspace=wsa)
+    mx.mx_quantize(fmt, B[s_last], out=qb, stats=stb, workspace=wsb)
+    mx.mx_gemm(fmt, qa, fmt, qb, c=C)
+    torch.cuda.synchronize()
+
     # fidelity: eq. (1) for A and B from the fused statistics, eq. (2) for the product
     st_a, st_b = mx.stats_to_dict(sta), mx.stats_to_dict(stb)
     qsnr = lambda st: 10 * np.log10(st["sig2"] / st["err2"])
@@ -119,6 +163,7 @@ def main():
     _, qsnr_ab = mx.mx_qsnr(R, C.float())
     del R
 
+    gt, qt = counted_traffic("gemm"), counted_traffic("quantize")
     out = {
         "metric": "quantize GB/s (% HBM peak) + MXFP4 GEMM TFLOP/s (% MFMA peak) on 1 MI355X",
         "value": round(quant_gbs, 1),
@@ -130,7 +175,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16->e2m1",
+        "dtype": "f32 (quantizer arithmetic), e2m1 x e2m1 -> f32 (MFMA)",
         "data": "synthetic",
         "config": {"workload": "W4A4 linear layer: MXFP4-quantize A bf16 8192x4096 N(0,1) and "
                                "B bf16 14336x4096 N(0,0.02^2) (1x32 E2M1, E8M0 floor, RTNE, fused stats), "
@@ -138,14 +183,21 @@ def main():
                    "M": M, "N": N, "K": K, "quant_bytes_per_step": quant_bytes},
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
                      "ms_a": round(qa_ms, 4), "ms_b": round(qb_ms, 4)},
+        "quantize_codes_only": {"gbs": round(quant0_gbs, 1), "frac_hbm_peak": round(quant0_gbs / HBM_PEAK_GBS, 4),
+                                "ms_a": round(qa0, 4), "ms_b": round(qb0, 4),
+                                "note": "same quantizer without the fused statistics; not part of the step"},
         "gemm": {"tflops": round(gemm_tflops, 1), "frac_fp4_peak": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                  "ms": round(g_ms, 4)},
         "roofline": {"bound": "mfma", "kernel": "block-scaled MXFP4 GEMM",
                      "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None},
-        "quantize_roofline": {"bound": "hbm", "kernel": "MXFP4 row quantizer (+ stats finalize)",
+                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+                     "traffic": None if gt is None else round(gt["traffic_bytes"])},
+        "quantize_roofline": {"bound": "hbm", "kernel": "MXFP4 row quantizer with fused statistics "
+                                                        "(+ statistics finalize), A and B",
                               "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                              "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+                              "traffic": None if qt is None else round(
+                                  sum(qt[t]["fetch_bytes"] + qt[t]["write_bytes"] for t in ("A", "B")))},
         "qsnr_db": {"A": round(qsnr(st_a), 4), "B": round(qsnr(st_b), 4), "AB": round(qsnr_ab, 4)},
         "cpu_baseline": None,
     }
@@ -154,10 +206,15 @@ def main():
         import oracle
         threads = len(os.sched_getaffinity(0))
         oracle.set_threads(threads)
-        t0 = time.perf_counter()
-        ra = oracle.quantize(a_np, oracle.Format())
-        rb = oracle.quantize(b_np, oracle.Format())
-        tq = time.perf_counter() - t0
+        # repeat the full quantization of A and B until about 10 s of CPU work
+        reps, tq = 0, 0.0
+        while tq < 10.0 and reps < 50:
+            t0 = time.perf_counter()
+            ra = oracle.quantize(a_np, oracle.Format())
+            rb = oracle.quantize(b_np, oracle.Format())
+            tq += time.perf_counter() - t0
+            reps += 1
+        tq /= reps
         rows = 256
         t0 = time.perf_counter()
         oracle.gemm_f64(ra["dequant"][:rows], rb["dequant"])
@@ -165,7 +222,7 @@ def main():
         out["cpu_baseline"] = {
             "value": round(quant_bytes / tq / 1e9, 4), "unit": "GB/s", "cores": oracle.get_threads(),
             "kind": "oracle",
-            "sample": f"full quantize of A and B ({(M + N) * K} elements, {tq:.2f} s); "
+            "sample": f"full quantize of A and B ({(M + N) * K} elements), {reps} times, {tq:.3f} s each; "
                       f"GEMM sample {rows}x{N}x{K} float64 in {tg:.2f} s",
             "gemm_tflops": round(2.0 * rows * N * K / tg / 1e12, 5),
         }

@@ -39,8 +39,6 @@ struct StatsOut {
 
 __global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64_t n, int64_t nelem,
                                                     StatsOut* out) {
-    __shared__ double sd[2][NT];
-    __shared__ unsigned long long su[3][NT];
     double s2 = 0, e2 = 0;
     unsigned long long nz = 0, fl = 0, zb = 0;
     // each thread owns the partials t, t + NT, ...; eight of them are loaded
@@ -59,20 +57,12 @@ __global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64
             s2 += q[u].sig2; e2 += q[u].err2; nz += q[u].nonzero; fl += q[u].flushed; zb += q[u].zero_blocks;
         }
     }
-    const int t = threadIdx.x;
-    sd[0][t] = s2; sd[1][t] = e2; su[0][t] = nz; su[1][t] = fl; su[2][t] = zb;
-    __syncthreads();
-    for (int w = NT / 2; w >= 1; w >>= 1) {
-        if (t < w) {
-            sd[0][t] += sd[0][t + w]; sd[1][t] += sd[1][t + w];
-            su[0][t] += su[0][t + w]; su[1][t] += su[1][t + w]; su[2][t] += su[2][t + w];
-        }
-        __syncthreads();
-    }
-    if (t == 0) {
+    // wave butterflies, then the waves in order: a fixed summation order
+    const StatPart r = block_sum<NT>(s2, e2, nz, fl, zb);
+    if (threadIdx.x == 0) {
         StatsOut o;
-        o.sig2 = sd[0][0]; o.err2 = sd[1][0]; o.n = nelem;
-        o.nonzero = (long long)su[0][0]; o.flushed = (long long)su[1][0]; o.zero_blocks = (long long)su[2][0];
+        o.sig2 = r.sig2; o.err2 = r.err2; o.n = nelem;
+        o.nonzero = (long long)r.nonzero; o.flushed = (long long)r.flushed; o.zero_blocks = (long long)r.zero_blocks;
         *out = o;
     }
 }
