@@ -281,7 +281,7 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (b->cols != K) return MX_ERR_ARG;
     if (c_dtype != MX_DTYPE_F32 && c_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
-    if (K % 128) return MX_ERR_UNSUPPORTED;
+    if (K % 32) return MX_ERR_UNSUPPORTED;
     if (ldc < N) return MX_ERR_ARG;
     if (M == 0 || N == 0) return MX_OK;
     if (K == 0) return MX_ERR_UNSUPPORTED;

@@ -61,20 +61,26 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
+    // K advances 128 per step; a 32-element block past the end of K (K is a
+    // multiple of 32 only) contributes zero codes under scale code 0
     for (int64_t k0 = 0; k0 < K; k0 += TK) {
         uint4 av[2][2], bv[2][2];
         int sa[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
+            uint32_t ca[2], cb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
-                av[i][kk] = *reinterpret_cast<const uint4*>(A + ra[i] * rowb + (k0 + 64 * kk + 32 * half) / 2);
-                bv[i][kk] = *reinterpret_cast<const uint4*>(B + rb[i] * rowb + (k0 + 64 * kk + 32 * half) / 2);
+                const int64_t kb = k0 / 32 + 2 * kk + half;   // this lane's K block
+                const bool in = kb < kblocks;
+                av[i][kk] = in ? *reinterpret_cast<const uint4*>(A + ra[i] * rowb + kb * 16) : make_uint4(0, 0, 0, 0);
+                bv[i][kk] = in ? *reinterpret_cast<const uint4*>(B + rb[i] * rowb + kb * 16) : make_uint4(0, 0, 0, 0);
+                ca[kk] = in ? SA[ra[i] * kblocks + kb] : 0u;
+                cb[kk] = in ? SB[rb[i] * kblocks + kb] : 0u;
             }
-            // the four E8M0 scales of this row over the 128-wide K step; this
-            // lane's block of chunk kk sits in byte 2*kk after the shift
-            sa[i] = (int)(*reinterpret_cast<const uint32_t*>(SA + ra[i] * kblocks + k0 / 32) >> (8 * half));
-            sb[i] = (int)(*reinterpret_cast<const uint32_t*>(SB + rb[i] * kblocks + k0 / 32) >> (8 * half));
+            // the scale of K block 2*kk + half in byte 2*kk: the op_sel value below
+            sa[i] = (int)(ca[0] | (ca[1] << 16));
+            sb[i] = (int)(cb[0] | (cb[1] << 16));
         }
 #pragma unroll
         for (int i = 0; i < 2; i++)

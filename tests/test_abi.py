@@ -133,7 +133,7 @@ def test_gemm_rejects_before_launch():
     a = mx.MxQTensor(1024, 2048, None, None, None, None, 64, 256)
     b = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 256)
     b_k = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 512)
-    b_k96 = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 96)
+    b_k80 = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 80)
     L = mx.lib()
     assert L.mx_gemm(ctypes.byref(bad), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
@@ -141,8 +141,9 @@ def test_gemm_rejects_before_launch():
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
     assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 16,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
-    assert L.mx_gemm(ctypes.byref(f), ctypes.byref(b_k96), ctypes.byref(f), ctypes.byref(b_k96), 0x10000, 32,
-                     mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    # K = 80 breaks the 1 x 32 block shape of the operands themselves
+    assert L.mx_gemm(ctypes.byref(f), ctypes.byref(b_k80), ctypes.byref(f), ctypes.byref(b_k80), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
     assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
 

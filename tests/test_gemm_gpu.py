@@ -40,7 +40,8 @@ def bf16_of(x64):
     return oracle.f32_to_bf16_bits(np.asarray(x64, np.float32))
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 136, 512), (128, 128, 128), (1, 1, 256), (257, 300, 384)])
+@pytest.mark.parametrize("M,N,K", [(200, 136, 512), (128, 128, 128), (1, 1, 256), (257, 300, 384),
+                                   (70, 90, 32), (130, 40, 96), (33, 300, 160), (256, 256, 224)])
 def test_exact_case_bit_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     ca = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -57,7 +58,7 @@ def test_exact_case_bit_exact(M, N, K):
     assert np.array_equal(got16, bf16_of(exact))
 
 
-@pytest.mark.parametrize("M,N,K", [(320, 192, 1024), (96, 520, 256)])
+@pytest.mark.parametrize("M,N,K", [(320, 192, 1024), (96, 520, 256), (200, 136, 96), (64, 64, 352)])
 def test_random_scales(M, N, K):
     rng = np.random.default_rng(K)
     ca = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
