@@ -190,7 +190,7 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  * C (M x N, row stride ldc elements) in bf16 (rounded to nearest even) or
  * fp32.  Runs on the gfx950 block-scaled FP4 matrix instructions.  Shapes:
  * K % 32 == 0, as the 1 x 32 blocks require (MX_ERR_ARG otherwise); K a
- * multiple of 128 takes the LDS-staged kernel, other multiples of 32 a
+ * multiple of 1024 takes the LDS-staged kernel, other multiples of 32 a
  * register-only one; any M, N.                                              */
 int mx_gemm(const mx_format *fa, const mx_qtensor *a, const mx_format *fb,
             const mx_qtensor *b, void *c, int64_t ldc, int c_dtype, void *stream);

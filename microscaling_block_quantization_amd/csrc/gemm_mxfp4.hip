@@ -111,32 +111,52 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
 
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 256 x 256 output tile per 256-thread workgroup (one wave per
-// SIMD, each wave 128 x 128 = 4 x 4 MFMA tiles, 256 fp32 accumulators per
-// lane).  K advances BK per stage; a stage holds the tile's A and B codes
-// (256 rows x BK/2 bytes each) and their E8M0 scales (256 rows x BK/32
-// bytes).  D stages form a ring in LDS: stage s + D - 1 is fetched by
-// LDS-DMA (global_load_lds, 16 bytes per lane for codes, 4 for scales) while
-// stage s is multiplied, so every load has D - 1 stages of MFMA work to land.
-// The 16-byte chunks of a code row are XOR-swizzled so that the ds_read_b128
-// operand reads of consecutive rows fall in distinct LDS bank groups.
+// Tiled kernel.  A workgroup of WGM x WGN waves computes a BM x BN output tile
+// (BM = WGM * 32 * TI, BN = WGN * 32 * TJ); each wave owns TI x TJ MFMA tiles
+// of 32 x 32 (16 fp32 accumulators per lane each).  K advances BK per stage; a
+// stage holds the tile's A and B codes (BM and BN rows x BK/2 bytes).  D
+// stages form a ring in LDS: stage s + D - 1 is fetched by LDS-DMA
+// (buffer_load ... lds, 16 bytes per lane) while stage s is multiplied, so
+// every load has D - 1 stages of MFMA work to land.  The 16-byte chunks of a
+// code row are XOR-swizzled so that the ds_read_b128 operand reads of
+// consecutive rows fall in distinct LDS bank groups.  The E8M0 scales travel
+// in groups of SG stages (SG * BK/32 contiguous bytes per row, 16 bytes per
+// lane): one scale byte per 16 code bytes would otherwise cost as many L2
+// requests as the codes themselves.  Two group buffers alternate in LDS.
+// With 8 waves (two per SIMD) one wave's MFMAs run while the other waits on
+// its DMA or LDS reads.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int BM = 256, BN = 256;
-
-template <int BK>
+template <int BK_, int WGM_, int WGN_, int TI_, int TJ_>
 struct Geo {
-    static constexpr int ROWB = BK / 2;            // code bytes per row per stage
-    static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
-    static constexpr int SPR = BK / 32;            // scale bytes per row per stage
-    static constexpr int ST_A = BM * ROWB;
-    static constexpr int ST_B = BN * ROWB;
-    static constexpr int ST_S = 256 * SPR;
-    static constexpr int STAGE = ST_A + ST_B + 2 * ST_S;
-    // physical chunk of logical chunk c in row r
+    static constexpr int BK = BK_, WGM = WGM_, WGN = WGN_, TI = TI_, TJ = TJ_;
+    static constexpr int NW = WGM * WGN;             // waves per workgroup
+    static constexpr int BM = WGM * 32 * TI, BN = WGN * 32 * TJ;
+    static constexpr int ROWB = BK / 2;              // code bytes per row per stage
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPL = 1024 / ROWB;          // rows per 1 KiB wave-load
+    static constexpr int SPR = BK / 32;              // scale bytes per row per stage
+    static constexpr int ST_A = BM * ROWB, ST_B = BN * ROWB;
+    static constexpr int OFF_B = ST_A;
+    static constexpr int STAGE = ST_A + ST_B;
+    static constexpr int SG = 8;                     // stages per scale group
+    static constexpr int SROW = SG * SPR;            // scale bytes per row per group (32)
+    static constexpr int SBUF = (BM + BN) * SROW;    // one group: A rows, then B rows
+    // wave-loads: code pieces of 1 KiB per stage, scale pieces of 1 KiB per
+    // group, dealt evenly to the waves (A's pieces first, then B's)
+    static constexpr int LA = ST_A / 1024, LB = ST_B / 1024;
+    static constexpr int PWC = (LA + LB) / NW;       // code DMA instructions per wave per stage
+    // a scale group is stored as 16-byte units (4 stages of one row) in
+    // [half][row] order, A then B: a piece of 64 units covers 64 rows of one half
+    static constexpr int LSA = 2 * BM / 64;          // A's scale pieces per group
+    static constexpr int PWS = 2 * (BM + BN) / 64 / NW;  // scale DMA instructions per wave per group
+    static_assert((LA + LB) % NW == 0 && (2 * (BM + BN) / 64) % NW == 0, "DMA must split evenly over the waves");
+    static_assert(SROW == 32 && BM % 64 == 0 && BN % 64 == 0, "two 16-byte units per scale row");
+    static_assert(CPR == 4 || CPR == 8, "BK of 128 or 256");
+    static constexpr int NOPS = TI + TJ;             // LDS reads per substep (A, then B fragments)
+    // physical chunk of logical chunk c in row r (an involution; depends on r mod 16)
     static __device__ __forceinline__ int phys(int r, int c) {
         if constexpr (CPR == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
         else return c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
@@ -158,174 +178,153 @@ struct Panels {
     int rowb, kblocks;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const uint8_t* base, int64_t row0, int64_t nrows, int rowbytes) {
-    const int64_t valid = nrows - row0 < 256 ? nrows - row0 : 256;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const uint8_t* base, int64_t row0, int64_t nrows, int rows,
+                                                        int rowbytes) {
+    const int64_t valid = nrows - row0 < rows ? nrows - row0 : rows;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * rowbytes), (short)0, (int)(valid * rowbytes),
                                              0x00020000);
 }
 
-// LDS-DMA of one stage.  A wave-load writes 1 KiB of LDS, lane l at bytes
-// [16 l, 16 l + 16), so each lane fetches the logical chunk that the swizzle
-// stores at its position; the swizzle of row r depends on r mod 16 only.
-template <int BK>
-__device__ __forceinline__ void stage_dma(uint8_t* __restrict__ lds, const Panels& P, int s, int wave, int lane) {
-    using G = Geo<BK>;
-    constexpr int RPL = 1024 / G::ROWB;              // rows per wave-load
-    constexpr int LOADS = G::ST_A / 1024 / 4;        // wave-loads per wave and operand
-    const int rin = lane / G::CPR, pc = lane % G::CPR;
-    const int vo0 = rin * P.rowb + (G::phys(rin, pc) << 4);            // even slots (RPL = 8) / all slots
-    const int vo1 = rin * P.rowb + (G::phys(rin + 8, pc) << 4);        // odd slots when RPL = 8
-#pragma unroll
-    for (int j = 0; j < LOADS; j++) {
-        const int slot = wave * LOADS + j;
-        const int vo = (RPL == 8 && (slot & 1)) ? vo1 : vo0;
-        const int so = slot * RPL * P.rowb + s * G::ROWB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(P.a, (lds_void*)(lds + slot * 1024), 16, vo, so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(P.b, (lds_void*)(lds + G::ST_A + slot * 1024), 16, vo, so, 0, 0);
-    }
-    constexpr int DPR = G::SPR / 4;                   // scale dwords per row per stage
-    constexpr int SLOADS = G::ST_S / 256 / 4;
-    const int svo = (lane / DPR) * P.kblocks + (lane % DPR) * 4;
-#pragma unroll
-    for (int j = 0; j < SLOADS; j++) {
-        const int slot = wave * SLOADS + j;
-        const int so = (slot * 64 / DPR) * P.kblocks + s * G::SPR;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(P.sa, (lds_void*)(lds + G::ST_A + G::ST_B + slot * 256), 4, svo, so,
-                                                 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(P.sb, (lds_void*)(lds + G::ST_A + G::ST_B + G::ST_S + slot * 256), 4,
-                                                 svo, so, 0, 0);
-    }
-}
-
-// operands of one 64-wide K substep: four A and four B 16-byte fragments and
-// the raw scale dwords of their rows
-struct Ops {
-    u32x4v a[4], b[4];
-    uint32_t sa[4], sb[4];
-};
-
-template <int BK>
-__device__ __forceinline__ void load_ops(Ops& o, const uint8_t* __restrict__ st, int t, int wm, int wn, int lrow,
-                                         int half) {
-    using G = Geo<BK>;
-    // rows i*32 apart share the swizzle (it depends on r mod 16), so each
-    // operand needs one lane address per substep and the four row tiles are
-    // immediate offsets from it
-    const int c = 2 * t + half;                      // this lane's 32-wide block in the stage
-    const int ra = wm * 128 + lrow, rb = wn * 128 + lrow;
-    const uint8_t* pa = st + ra * G::ROWB + (G::phys(ra, c) << 4);
-    const uint8_t* pb = st + G::ST_A + rb * G::ROWB + (G::phys(rb, c) << 4);
-    const uint8_t* qa = st + G::ST_A + G::ST_B + ra * G::SPR + 4 * (t >> 1);
-    const uint8_t* qb = st + G::ST_A + G::ST_B + G::ST_S + rb * G::SPR + 4 * (t >> 1);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        o.a[i] = *reinterpret_cast<const u32x4v*>(pa + i * 32 * G::ROWB);
-        o.b[i] = *reinterpret_cast<const u32x4v*>(pb + i * 32 * G::ROWB);
-        o.sa[i] = *reinterpret_cast<const uint32_t*>(qa + i * 32 * G::SPR);
-        o.sb[i] = *reinterpret_cast<const uint32_t*>(qb + i * 32 * G::SPR);
-    }
-}
-
-// 16 MFMAs of one substep.  After the shift by 8*half this lane's scale byte
-// (block 2t + half of the stage) is byte 2*(t&1): the op_sel value.
-template <int T1>
-__device__ __forceinline__ void mma(const Ops& o, v16f (&acc)[4][4], int half) {
-    int xa[4], xb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        xa[i] = (int)(o.sa[i] >> (8 * half));
-        xb[i] = (int)(o.sb[i] >> (8 * half));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(o.a[i]), op8(o.b[j]), acc[i][j], 4, 4,
-                                                                       2 * T1, xa[i], 2 * T1, xb[j]);
-}
-
-// scheduling masks of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DSR = 0x100;
-
-// One substep group in a fixed instruction order: MFMA k of `cur`, then LDS
-// read k of the next operands, then DMA instruction k of a later stage, with
-// a scheduling fence after each step.  Every DMA instruction holds the wave
-// at the texture unit for a while and the MFMA in flight hides it; every LDS
-// read has the rest of the group to land.
+// DMA instruction k (0 .. L-1) of this wave for stage s into the stage buffer
+// `lds`.  Code piece g covers rows [g*RPL, g*RPL + RPL) of its operand; lane l
+// writes LDS bytes [16 l, 16 l + 16) of the piece, i.e. row g*RPL + l/CPR at
+// physical chunk l%CPR, so it fetches the logical chunk the swizzle stores
+// there.  Scale piece h covers 64/DPR rows, one dword per lane.
 struct DmaSlot {
     uint8_t* lds;          // uniform LDS destination (goes to M0)
-    const Panels* P;
+    Panels P;              // the operand panels, or their zero-size twins
     int s, wave, lane;
 };
 
-template <int BK>
+template <class G>
 __device__ __forceinline__ void dma_piece(const DmaSlot& d, int k) {
-    using G = Geo<BK>;
-    constexpr int RPL = 1024 / G::ROWB;
-    constexpr int LOADS = G::ST_A / 1024 / 4;
+    const int g = d.wave * G::PWC + k;              // uniform
+    const bool isb = g >= G::LA;
+    const int slot = isb ? g - G::LA : g;
     const int rin = d.lane / G::CPR, pc = d.lane % G::CPR;
-    if (k < 2 * LOADS) {
-        const int j = k >> 1, slot = d.wave * LOADS + j;
-        const int vo = rin * d.P->rowb + (G::phys((RPL == 8 && (slot & 1)) ? rin + 8 : rin, pc) << 4);
-        const int so = slot * RPL * d.P->rowb + d.s * G::ROWB;
-        if (k & 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.P->b, (lds_void*)(d.lds + G::ST_A + slot * 1024), 16, vo, so, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.P->a, (lds_void*)(d.lds + slot * 1024), 16, vo, so, 0, 0);
-    } else {
-        constexpr int DPR = G::SPR / 4;
-        constexpr int SLOADS = G::ST_S / 256 / 4;
-        const int kk = k - 2 * LOADS, j = kk >> 1, slot = d.wave * SLOADS + j;
-        const int svo = (d.lane / DPR) * d.P->kblocks + (d.lane % DPR) * 4;
-        const int so = (slot * 64 / DPR) * d.P->kblocks + d.s * G::SPR;
-        if (kk & 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.P->sb, (lds_void*)(d.lds + G::ST_A + G::ST_B + G::ST_S + slot * 256),
-                                                     4, svo, so, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.P->sa, (lds_void*)(d.lds + G::ST_A + G::ST_B + slot * 256), 4,
-                                                     svo, so, 0, 0);
-    }
+    const int row = slot * G::RPL + rin;
+    const int vo = rin * d.P.rowb + (G::phys(row, pc) << 4);
+    const int so = slot * G::RPL * d.P.rowb + d.s * G::ROWB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isb ? d.P.b : d.P.a,
+                                             (lds_void*)(d.lds + (isb ? G::OFF_B : 0) + slot * 1024), 16, vo, so, 0, 0);
 }
 
-// LDS read k (0..11) of the operands of substep t: k = 0..3 A fragments,
-// 4..7 B fragments, 8..11 scale dwords (A, B pairs)
-template <int BK>
-__device__ __forceinline__ void ops_piece(Ops& o, const uint8_t* __restrict__ st, int t, int wm, int wn, int lrow,
-                                          int half, int k) {
-    using G = Geo<BK>;
-    const int c = 2 * t + half;
-    const int ra = wm * 128 + lrow, rb = wn * 128 + lrow;
-    if (k < 4) {
-        o.a[k] = *reinterpret_cast<const u32x4v*>(st + ra * G::ROWB + (G::phys(ra, c) << 4) + k * 32 * G::ROWB);
-    } else if (k < 8) {
-        o.b[k - 4] = *reinterpret_cast<const u32x4v*>(st + G::ST_A + rb * G::ROWB + (G::phys(rb, c) << 4) +
-                                                      (k - 4) * 32 * G::ROWB);
-    } else {
-        const int i = k - 8;
-        o.sa[i] = *reinterpret_cast<const uint32_t*>(st + G::ST_A + G::ST_B + ra * G::SPR + 4 * (t >> 1) +
-                                                      i * 32 * G::SPR);
-        o.sb[i] = *reinterpret_cast<const uint32_t*>(st + G::ST_A + G::ST_B + G::ST_S + rb * G::SPR + 4 * (t >> 1) +
-                                                      i * 32 * G::SPR);
-    }
-}
-
-template <int BK, int T1, int NV>
-__device__ __forceinline__ void substep(const Ops& cur, v16f (&acc)[4][4], Ops& nxt, const uint8_t* __restrict__ st,
-                                      int t, int wm, int wn, int lrow, int half, const DmaSlot* d) {
-    int xa[4], xb[4];
+template <class G>
+__device__ __forceinline__ void stage_dma(const DmaSlot& d) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        xa[i] = (int)(cur.sa[i] >> (8 * half));
-        xb[i] = (int)(cur.sb[i] >> (8 * half));
+    for (int k = 0; k < G::PWC; k++) dma_piece<G>(d, k);
+}
+
+// DMA of scale group `grp` (stages grp*SG ...) into the group buffer `lds`:
+// piece h of an operand holds half h/(R/64) of rows 64*(h%(R/64)) + lane
+// (R rows), lane l at LDS bytes [16 l, 16 l + 16) of the piece.
+template <class G>
+__device__ __forceinline__ void scale_dma(uint8_t* lds, __amdgpu_buffer_rsrc_t sa, __amdgpu_buffer_rsrc_t sb,
+                                          int kblocks, int grp, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < G::PWS; k++) {
+        const int h = wave * G::PWS + k;            // uniform
+        const bool isb = h >= G::LSA;
+        const int slot = isb ? h - G::LSA : h;
+        const int per_half = (isb ? G::BN : G::BM) / 64;
+        const int vo = lane * kblocks;
+        const int so = (slot % per_half) * 64 * kblocks + grp * G::SROW + (slot / per_half) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isb ? sb : sa,
+                                                 (lds_void*)(lds + (isb ? G::BM * G::SROW : 0) + slot * 1024), 16, vo,
+                                                 so, 0, 0);
     }
+}
+
+// operands of one 64-wide K substep: TI A and TJ B 16-byte fragments
+template <class G>
+struct Ops {
+    u32x4v a[G::TI], b[G::TJ];
+};
+
+// the scale dwords of this lane's rows for 4 consecutive stages (one 16-byte
+// unit per row tile, A's then B's), read once per 4 stages and shifted by
+// 8*half: then byte 0 is this lane's block of the stage's first substep and
+// byte 2 that of its second (the op_sel values 0 and 2)
+template <class G>
+struct Scl {
+    u32x4v q[G::TI + G::TJ];
+};
+
+template <class G>
+__device__ __forceinline__ void load_scl(Scl<G>& o, const uint8_t* __restrict__ buf, int hf, int ra, int rb,
+                                         int half) {
+#pragma unroll
+    for (int i = 0; i < G::TI; i++)
+        o.q[i] = *reinterpret_cast<const u32x4v*>(buf + (hf * G::BM + ra + 32 * i) * 16) >> (8u * half);
+#pragma unroll
+    for (int j = 0; j < G::TJ; j++)
+        o.q[G::TI + j] =
+            *reinterpret_cast<const u32x4v*>(buf + G::BM * G::SROW + (hf * G::BN + rb + 32 * j) * 16) >> (8u * half);
+}
+
+// LDS read k (0 .. NOPS-1) of the operands of substep t: A fragments, B
+// fragments, A scale dwords, B scale dwords.  Rows i*32 apart share the
+// swizzle, so the row tiles are immediate offsets from one lane address.
+template <class G>
+__device__ __forceinline__ void ops_piece(Ops<G>& o, const uint8_t* __restrict__ st, int t, int ra, int rb, int half,
+                                          int k) {
+    const int c = 2 * t + half;                      // this lane's 32-wide block in the stage
+    if (k < G::TI) {
+        o.a[k] = *reinterpret_cast<const u32x4v*>(st + ra * G::ROWB + (G::phys(ra, c) << 4) + k * 32 * G::ROWB);
+    } else {
+        const int j = k - G::TI;
+        o.b[j] = *reinterpret_cast<const u32x4v*>(st + G::OFF_B + rb * G::ROWB + (G::phys(rb, c) << 4) +
+                                                  j * 32 * G::ROWB);
+    }
+}
+
+template <class G>
+__device__ __forceinline__ void load_ops(Ops<G>& o, const uint8_t* __restrict__ st, int t, int ra, int rb, int half) {
+#pragma unroll
+    for (int k = 0; k < G::NOPS; k++) ops_piece<G>(o, st, t, ra, rb, half, k);
+}
+
+// One substep in a fixed instruction order: MFMA k of `cur`, then its share of
+// the LDS reads of the next operands and of the DMA of a later stage, with a
+// scheduling fence after each step.  A DMA instruction holds the wave at the
+// texture unit for a while and the MFMA in flight hides it; every LDS read
+// has the rest of the substep to land.  After the shift by 8*half this lane's
+// scale byte (block 2t + half of the stage) is byte 2*(t&1): the op_sel value.
+// this stage's scale dwords: component s % 4 of the registers of Scl
+template <class G>
+struct Cur {
+    int x[G::TI + G::TJ];
+};
+
+template <class G>
+__device__ __forceinline__ void pick(Cur<G>& c, const Scl<G>& sc, int u) {
+#pragma unroll
+    for (int i = 0; i < G::TI + G::TJ; i++) {
+        const u32x4v q = sc.q[i];
+        c.x[i] = (int)(u == 0 ? q.x : u == 1 ? q.y : u == 2 ? q.z : q.w);
+    }
+}
+
+template <class G, int T1, int NV>
+__device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16f (&acc)[G::TI][G::TJ], Ops<G>& nxt,
+                                        const uint8_t* __restrict__ st, int t, int ra, int rb, int half,
+                                        const DmaSlot* d) {
+    constexpr int NM = G::TI * G::TJ;
+    int xa[G::TI], xb[G::TJ];
+#pragma unroll
+    for (int i = 0; i < G::TI; i++) xa[i] = sc.x[i];
+#pragma unroll
+    for (int j = 0; j < G::TJ; j++) xb[j] = sc.x[G::TI + j];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
-        const int i = k >> 2, j = k & 3;
+    for (int k = 0; k < NM; k++) {
+        const int i = k / G::TJ, j = k % G::TJ;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(cur.a[i]), op8(cur.b[j]), acc[i][j], 4, 4,
                                                                    2 * T1, xa[i], 2 * T1, xb[j]);
-        if (k < 12) ops_piece<BK>(nxt, st, t, wm, wn, lrow, half, k);
-        if (k < NV) dma_piece<BK>(*d, k);
+#pragma unroll
+        for (int q = k * G::NOPS / NM; q < (k + 1) * G::NOPS / NM; q++) ops_piece<G>(nxt, st, t, ra, rb, half, q);
+#pragma unroll
+        for (int q = k * NV / NM; q < (k + 1) * NV / NM; q++) dma_piece<G>(*d, q);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -346,37 +345,41 @@ __device__ __forceinline__ void bar() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// the stage handover: start the DMA of a later stage into `dma` while the
-// last substep of the current stage multiplies and the first operands of the
-// next stage are read from `nxt`.  The buffers are distinct restrict-qualified
-// objects here, so the operand reads carry no dependence on the DMA.
-template <int BK, int T1>
-__device__ __forceinline__ void handover(const uint8_t* __restrict__ nxt, const Ops& cur, v16f (&acc)[4][4], Ops& o,
-                                         int wm, int wn, int lrow, int half) {
-    substep<BK, T1, 0>(cur, acc, o, nxt, 0, wm, wn, lrow, half, nullptr);
+// the stage handover: the last substep of the current stage multiplies while
+// the first operands of the next stage are read from `nxt`.  The buffers are
+// distinct restrict-qualified objects here, so the operand reads carry no
+// dependence on the DMA in flight.
+template <class G, int T1>
+__device__ __forceinline__ void handover(const uint8_t* __restrict__ nxt, const Ops<G>& cur, const Cur<G>& sc,
+                                         v16f (&acc)[G::TI][G::TJ], Ops<G>& o, int ra, int rb, int half) {
+    substep<G, T1, 0>(cur, sc, acc, o, nxt, 0, ra, rb, half, nullptr);
 }
 
-template <bool CBF16, int BK, int D>
-__global__ __launch_bounds__(256, 1) void k_gemm_tiled(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
-                                                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
-                                                       void* __restrict__ C, int64_t M, int64_t N, int64_t K,
-                                                       int64_t ldc) {
-    using G = Geo<BK>;
+template <bool CBF16, class G, int D>
+__global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ SA,
+                                                              const uint8_t* __restrict__ B,
+                                                              const uint8_t* __restrict__ SB, void* __restrict__ C,
+                                                              int64_t M, int64_t N, int64_t K, int64_t ldc) {
     static_assert(D >= 3 && D <= 4, "ring depth: the handover waits for the next stage while D - 3 more are in flight");
-    constexpr int NSUB = BK / 64;
-    constexpr int L = 2 * (G::ST_A / 1024 / 4) + 2 * (G::ST_S / 256 / 4);   // DMA ops per wave per stage
-    constexpr int CROW = 128 * 2 + 16;               // padded bf16 row of a wave's C tile in LDS
-    static_assert(D * G::STAGE >= 4 * 128 * CROW, "C staging must fit in the ring");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
+    static_assert(G::BK == 128, "the loop below is written for two substeps per stage");
+    constexpr int TI = G::TI, TJ = G::TJ, L = G::PWC, SG = G::SG;
+    static_assert(SG > D - 2, "at most one scale group is issued among the stages in flight");
+    constexpr int CROW = 64 * TJ + 16;               // padded bf16 row of a wave's 32-row C strip in LDS
+    static_assert(D * G::STAGE >= G::NW * 32 * CROW, "C staging must fit in the ring");
+    // the code ring, then the two scale-group buffers
+    __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE + 2 * G::SBUF];
+    uint8_t* const sgb = smem + D * G::STAGE;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, lrow = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / G::WGN, wn = wave % G::WGN;
+    const int ra = wm * 32 * TI + lrow, rb = wn * 32 * TJ + lrow;   // this lane's operand rows in the tile
 
     // XCD-aware, grouped tile order: workgroups are dealt to the 8 XCDs round
     // robin, so consecutive tiles of the grouped order go to one XCD and share
     // A and B panels in its L2
-    const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+    const int tm = (int)((M + G::BM - 1) / G::BM), tn = (int)((N + G::BN - 1) / G::BN);
     const int T = tm * tn;
     int bid = blockIdx.x;
     if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
@@ -385,23 +388,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled(const uint8_t* __restrict
     const int first = group * GM;
     const int gsz = (tm - first) < GM ? (tm - first) : GM;
     const int in_g = bid - group * GM * tn;
-    const int64_t m0 = (int64_t)(first + in_g % gsz) * BM;
-    const int64_t n0 = (int64_t)(in_g / gsz) * BN;
+    const int64_t m0 = (int64_t)(first + in_g % gsz) * G::BM;
+    const int64_t n0 = (int64_t)(in_g / gsz) * G::BN;
 
-    const int nst = (int)(K / BK);
+    const int nst = (int)(K / G::BK);
     Panels P;
     P.rowb = (int)(K / 2);
     P.kblocks = (int)(K / 32);
-    P.a = panel(A, m0, M, P.rowb);
-    P.b = panel(B, n0, N, P.rowb);
-    P.sa = panel(SA, m0, M, P.kblocks);
-    P.sb = panel(SB, n0, N, P.kblocks);
+    P.a = panel(A, m0, M, G::BM, P.rowb);
+    P.b = panel(B, n0, N, G::BN, P.rowb);
+    P.sa = panel(SA, m0, M, G::BM, P.kblocks);
+    P.sb = panel(SB, n0, N, G::BN, P.kblocks);
 
-    v16f acc[4][4];
+    v16f acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < TJ; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
@@ -415,90 +418,124 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled(const uint8_t* __restrict
     Z.sa = __builtin_amdgcn_make_buffer_rsrc((void*)SA, (short)0, 0, 0x00020000);
     Z.sb = __builtin_amdgcn_make_buffer_rsrc((void*)SB, (short)0, 0, 0x00020000);
 
+    // scale group 0 goes first, ahead of the codes of stage 0, so waiting for
+    // a stage's codes also covers its scales (vector memory completes in order)
+    scale_dma<G>(sgb, P.sa, P.sb, P.kblocks, 0, wave, lane);
 #pragma unroll
-    for (int p = 0; p < D - 1; p++) stage_dma<BK>(smem + p * G::STAGE, p < nst ? P : Z, p, wave, lane);
-    wait_vm<(D - 2) * L>();                          // stage 0 has landed
+    for (int p = 0; p < D - 1; p++) {
+        const DmaSlot d = {smem + p * G::STAGE, p < nst ? P : Z, p, wave, lane};
+        stage_dma<G>(d);
+    }
+    wait_vm<(D - 2) * L>();                          // stage 0 and scale group 0 have landed
     bar();
-    // two operand sets in ping-pong: X holds even substeps, Y odd ones
-    Ops X, Y;
-    load_ops<BK>(X, smem, 0, wm, wn, lrow, half);
-    static_assert(NSUB == 2, "the loop below is written for two substeps per stage");
+    // two operand sets in ping-pong: X holds even substeps, Y odd ones; the
+    // scale registers hold 4 stages and are refilled at every 4th stage
+    Ops<G> X, Y;
+    Scl<G> S;
+    Cur<G> Q;
+    load_ops<G>(X, smem, 0, ra, rb, half);
     for (int s = 0; s < nst; s++) {
         const uint8_t* st = smem + (s % D) * G::STAGE;
+        if ((s & 3) == 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
+        pick<G>(Q, S, s & 3);
         // substep 0 of stage s, the reads of substep 1 and the DMA of stage
         // s + D - 1 into the buffer of stage s - 1 (every wave finished its
-        // reads of it before the previous barrier)
+        // reads of it before the previous barrier).  A stage that opens a
+        // scale group is preceded by that group's DMA into the buffer the
+        // group before last used, long since read.
         const int nx = s + D - 1;
-        const DmaSlot d = {smem + (nx % D) * G::STAGE, nx < nst ? &P : &Z, nx, wave, lane};
-        substep<BK, 0, L>(X, acc, Y, st, 1, wm, wn, lrow, half, &d);
-        // stage s + 1 must have landed before its first operands are read
-        // (after the last stage the read is of a buffer that is never used)
-        wait_vm<(D - 2) * L>();
+        if (nx % SG == 0)
+            scale_dma<G>(sgb + ((nx / SG) & 1) * G::SBUF, nx < nst ? P.sa : Z.sa, nx < nst ? P.sb : Z.sb, P.kblocks,
+                         nx / SG, wave, lane);
+        const DmaSlot d = {smem + (nx % D) * G::STAGE, nx < nst ? P : Z, nx, wave, lane};
+        substep<G, 0, L>(X, Q, acc, Y, st, 1, ra, rb, half, &d);
+        // stage s + 1 (and its scales) must have landed before its first
+        // operands are read; what may stay in flight is the DMA of the later
+        // stages, plus one scale group if one of them opens a group (after the
+        // last stage the read is of a buffer that is never used)
+        bool extra = false;
+#pragma unroll
+        for (int q = 2; q <= D - 1; q++) extra = extra || ((s + q) % SG == 0);
+        if (extra) wait_vm<(D - 2) * L + G::PWS>();
+        else wait_vm<(D - 2) * L>();
         bar();
-        handover<BK, 1>(smem + ((s + 1) % D) * G::STAGE, Y, acc, X, wm, wn, lrow, half);
+        handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
     }
     wait_vm<0>();
 
     if constexpr (CBF16) {
-        // stage each wave's 128 x 128 tile as bf16 rows in LDS, then write C
-        // with 16-byte stores (each row segment of a wave-store is contiguous)
+        // each wave stages one 32-row strip of its tile at a time as bf16 rows
+        // in a private LDS area, then writes C with 16-byte stores (a row
+        // segment of a wave-store is contiguous).  LDS operations of one wave
+        // complete in order, so the strips need no barrier between them.
         __syncthreads();
-        uint8_t* ct = smem + wave * 128 * CROW;
+        uint8_t* ct = smem + wave * 32 * CROW;
+        constexpr int CPRC = 4 * TJ;                 // 16-byte chunks per strip row
+        constexpr int RPI = 64 / CPRC;               // strip rows per wave-store
+        const bool vec = (ldc % 8) == 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < TI; i++) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < TJ; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     typedef float f2 __attribute__((ext_vector_type(2)));
                     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
                     const f2 f = {acc[i][j][r], acc[i][j][r + 1]};
                     const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
-                    const int ml = i * 32 + 8 * (r / 4) + 4 * half + (r % 4), nl = j * 32 + lrow;
+                    const int ml = 8 * (r / 4) + 4 * half + (r % 4), nl = j * 32 + lrow;
                     *reinterpret_cast<uint16_t*>(ct + ml * CROW + nl * 2) = (uint16_t)w;
                     *reinterpret_cast<uint16_t*>(ct + (ml + 1) * CROW + nl * 2) = (uint16_t)(w >> 16);
                 }
-        __syncthreads();
-        const bool vec = (ldc % 8) == 0;
-#pragma unroll 4
-        for (int q = 0; q < 32; q++) {
-            const int row = q * 4 + (lane >> 4), chunk = lane & 15;
-            const int64_t m = m0 + wm * 128 + row, n = n0 + wn * 128 + chunk * 8;
-            if (m >= M || n >= N) continue;
-            const u32x4v v = *reinterpret_cast<const u32x4v*>(ct + row * CROW + chunk * 16);
-            uint16_t* dst = static_cast<uint16_t*>(C) + m * ldc + n;
-            if (vec && n + 8 <= N) {
-                *reinterpret_cast<u32x4v*>(dst) = v;
-            } else {
-                const uint32_t e[4] = {v.x, v.y, v.z, v.w};
-                for (int k = 0; k < 8 && n + k < N; k++) dst[k] = (uint16_t)(e[k >> 1] >> (16 * (k & 1)));
+#pragma unroll
+            for (int q = 0; q < 32 / RPI; q++) {
+                const int row = q * RPI + lane / CPRC, chunk = lane % CPRC;
+                const int64_t m = m0 + wm * 32 * TI + i * 32 + row, n = n0 + wn * 32 * TJ + chunk * 8;
+                const u32x4v v = *reinterpret_cast<const u32x4v*>(ct + row * CROW + chunk * 16);
+                if (m >= M || n >= N) continue;
+                uint16_t* dst = static_cast<uint16_t*>(C) + m * ldc + n;
+                if (vec && n + 8 <= N) {
+                    *reinterpret_cast<u32x4v*>(dst) = v;
+                } else {
+                    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+                    for (int k = 0; k < 8 && n + k < N; k++) dst[k] = (uint16_t)(e[k >> 1] >> (16 * (k & 1)));
+                }
             }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < TI; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int64_t n = n0 + wn * 128 + j * 32 + lrow;
+            for (int j = 0; j < TJ; j++) {
+                const int64_t n = n0 + wn * 32 * TJ + j * 32 + lrow;
                 if (n >= N) continue;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                    const int64_t m = m0 + wm * 32 * TI + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                     if (m < M) static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
                 }
             }
     }
 }
 
+#ifndef GEMM_WAVES
+#define GEMM_WAVES 8
+#endif
+// 4 waves: 2 x 2 waves of 4 x 4 MFMA tiles; 8 waves: 2 x 4 waves of 4 x 2
+using GemmGeo = Geo<GEMM_BK, 2, GEMM_WAVES / 2, 4, GEMM_WAVES == 8 ? 2 : 4>;
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c,
                        int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    if (K % GEMM_BK == 0) {
-        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        if (c_bf16) k_gemm_tiled<true, GEMM_BK, GEMM_D><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
-        else k_gemm_tiled<false, GEMM_BK, GEMM_D><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    // the tiled kernel fetches scales in 32-byte row groups (8 stages of 128):
+    // with K a multiple of 1024 every scale row starts 32-byte aligned
+    if (K % 1024 == 0) {
+        using G = GemmGeo;
+        const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
+        if (c_bf16) k_gemm_tiled<true, G, GEMM_D><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+        else k_gemm_tiled<false, G, GEMM_D><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));

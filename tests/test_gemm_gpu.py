@@ -41,7 +41,8 @@ def bf16_of(x64):
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 136, 512), (128, 128, 128), (1, 1, 256), (257, 300, 384),
-                                   (70, 90, 32), (130, 40, 96), (33, 300, 160), (256, 256, 224)])
+                                   (70, 90, 32), (130, 40, 96), (33, 300, 160), (256, 256, 224),
+                                   (257, 300, 1024), (200, 520, 2048), (300, 257, 3072), (512, 256, 1024)])
 def test_exact_case_bit_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     ca = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
@@ -58,7 +59,8 @@ def test_exact_case_bit_exact(M, N, K):
     assert np.array_equal(got16, bf16_of(exact))
 
 
-@pytest.mark.parametrize("M,N,K", [(320, 192, 1024), (96, 520, 256), (200, 136, 96), (64, 64, 352)])
+@pytest.mark.parametrize("M,N,K", [(320, 192, 1024), (96, 520, 256), (200, 136, 96), (64, 64, 352),
+                                   (130, 700, 3072), (513, 260, 2048)])
 def test_random_scales(M, N, K):
     rng = np.random.default_rng(K)
     ca = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
