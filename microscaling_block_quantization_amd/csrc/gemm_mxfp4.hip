@@ -355,7 +355,75 @@ __device__ __forceinline__ void handover(const uint8_t* __restrict__ nxt, const 
     substep<G, T1, 0>(cur, sc, acc, o, nxt, 0, ra, rb, half, nullptr);
 }
 
-template <bool CBF16, class G, int D>
+// one C tile's store path: bf16 rows staged per 16-row strip in a private
+// LDS area of each wave (LDS operations of one wave complete in order, so the
+// strips need no barrier), then written with 16-byte stores.  With `exact`,
+// every wave issues exactly NSTORE buffer stores, lanes outside C aiming past
+// the resource (the count matters to the in-order vector-memory waits of the
+// next tile); otherwise stores are per element where a 16-byte chunk would
+// cross the end of a row.
+template <class G>
+struct CStore {
+    static constexpr int TI = G::TI, TJ = G::TJ;
+    static constexpr int SROWS = 16;                 // rows per strip
+    static constexpr int CROW = 64 * TJ + 16;        // padded bf16 strip row
+    static constexpr int CPRC = 4 * TJ;              // 16-byte chunks per strip row
+    static constexpr int RPI = 64 / CPRC;            // strip rows per wave-store
+    static constexpr int NSTORE = TI * (32 / SROWS) * (SROWS / RPI);
+    static constexpr int AREA = SROWS * CROW;        // LDS bytes per wave
+};
+
+template <class G, bool EXACT>
+__device__ __forceinline__ void store_c_bf16(const v16f (&acc)[G::TI][G::TJ], uint8_t* ct, void* C, int64_t m0,
+                                             int64_t n0, int64_t M, int64_t N, int64_t ldc, int wm, int wn, int lane,
+                                             int half, int lrow) {
+    using S = CStore<G>;
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const int64_t vrows = M - m0 < G::BM ? M - m0 : G::BM;
+    uint8_t* cbase = static_cast<uint8_t*>(C) + m0 * ldc * 2;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(cbase, (short)0, (int)(vrows * ldc * 2),
+                                                                        0x00020000);
+#pragma unroll
+    for (int i = 0; i < S::TI; i++)
+#pragma unroll
+        for (int hs = 0; hs < 32 / S::SROWS; hs++) {
+#pragma unroll
+            for (int j = 0; j < S::TJ; j++)
+#pragma unroll
+                for (int r = 8 * hs; r < 8 * hs + 8; r += 2) {
+                    const f2 f = {acc[i][j][r], acc[i][j][r + 1]};
+                    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
+                    const int ml = 8 * (r / 4) + 4 * half + (r % 4) - S::SROWS * hs, nl = j * 32 + lrow;
+                    *reinterpret_cast<uint16_t*>(ct + ml * S::CROW + nl * 2) = (uint16_t)w;
+                    *reinterpret_cast<uint16_t*>(ct + (ml + 1) * S::CROW + nl * 2) = (uint16_t)(w >> 16);
+                }
+#pragma unroll
+            for (int q = 0; q < S::SROWS / S::RPI; q++) {
+                const int row = q * S::RPI + lane / S::CPRC, chunk = lane % S::CPRC;
+                const int mt = wm * 32 * S::TI + i * 32 + hs * S::SROWS + row;       // row in the tile
+                const int64_t n = n0 + wn * 32 * S::TJ + chunk * 8;
+                const u32x4v v = *reinterpret_cast<const u32x4v*>(ct + row * S::CROW + chunk * 16);
+                if constexpr (EXACT) {
+                    const int off = n < N ? (int)(mt * ldc * 2 + n * 2) : (int)0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+                } else {
+                    const int64_t m = m0 + mt;
+                    if (m >= M || n >= N) continue;
+                    uint16_t* dst = static_cast<uint16_t*>(C) + m * ldc + n;
+                    if (n + 8 <= N && (ldc % 8) == 0) {
+                        *reinterpret_cast<u32x4v*>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; k++)
+                            if (n + k < N) dst[k] = (uint16_t)(v[k >> 1] >> (16 * (k & 1)));
+                    }
+                }
+            }
+        }
+}
+
+template <bool CBF16, bool EXACT, class G, int D>
 __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __restrict__ A,
                                                               const uint8_t* __restrict__ SA,
                                                               const uint8_t* __restrict__ B,
@@ -364,9 +432,11 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
     static_assert(D >= 3 && D <= 4, "ring depth: the handover waits for the next stage while D - 3 more are in flight");
     static_assert(G::BK == 128, "the loop below is written for two substeps per stage");
     constexpr int TI = G::TI, TJ = G::TJ, L = G::PWC, SG = G::SG;
-    static_assert(SG > D - 2, "at most one scale group is issued among the stages in flight");
-    constexpr int CROW = 64 * TJ + 16;               // padded bf16 row of a wave's 32-row C strip in LDS
-    static_assert(D * G::STAGE >= G::NW * 32 * CROW, "C staging must fit in the ring");
+    using CS = CStore<G>;
+    constexpr int NSTORE = CS::NSTORE;
+    static_assert(SG > 2 * D - 4, "no scale group opens among the stages that overlap the previous tile's stores");
+    static_assert((D - 2) * L + G::PWS <= 63 && (D - 2) * L + NSTORE <= 63, "vector-memory wait counts fit vmcnt");
+    static_assert(G::NW * CS::AREA <= G::STAGE, "C strips are staged in the last ring slot");
     // the code ring, then the two scale-group buffers
     __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE + 2 * G::SBUF];
     uint8_t* const sgb = smem + D * G::STAGE;
@@ -375,30 +445,68 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
     const int half = lane >> 5, lrow = lane & 31;
     const int wm = wave / G::WGN, wn = wave % G::WGN;
     const int ra = wm * 32 * TI + lrow, rb = wn * 32 * TJ + lrow;   // this lane's operand rows in the tile
+    uint8_t* const ct = smem + (D - 1) * G::STAGE + wave * CS::AREA;
 
-    // XCD-aware, grouped tile order: workgroups are dealt to the 8 XCDs round
-    // robin, so consecutive tiles of the grouped order go to one XCD and share
-    // A and B panels in its L2
+    // XCD-aware, grouped tile order: workgroup slots are dealt to the 8 XCDs
+    // round robin, so consecutive tiles of the grouped order go to one XCD and
+    // share A and B panels in its L2.  The workgroups are persistent: slot
+    // blockIdx.x + k * gridDim.x is a workgroup's k-th tile.
     const int tm = (int)((M + G::BM - 1) / G::BM), tn = (int)((N + G::BN - 1) / G::BN);
     const int T = tm * tn;
-    int bid = blockIdx.x;
-    if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
-    constexpr int GM = 8;
-    const int group = bid / (GM * tn);
-    const int first = group * GM;
-    const int gsz = (tm - first) < GM ? (tm - first) : GM;
-    const int in_g = bid - group * GM * tn;
-    const int64_t m0 = (int64_t)(first + in_g % gsz) * G::BM;
-    const int64_t n0 = (int64_t)(in_g / gsz) * G::BN;
-
+    auto tile_of = [&](int lin, int64_t& m0, int64_t& n0) {
+        int bid = lin;
+        if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+        constexpr int GM = 8;
+        const int group = bid / (GM * tn);
+        const int first = group * GM;
+        const int gsz = (tm - first) < GM ? (tm - first) : GM;
+        const int in_g = bid - group * GM * tn;
+        m0 = (int64_t)(first + in_g % gsz) * G::BM;
+        n0 = (int64_t)(in_g / gsz) * G::BN;
+    };
     const int nst = (int)(K / G::BK);
-    Panels P;
-    P.rowb = (int)(K / 2);
-    P.kblocks = (int)(K / 32);
-    P.a = panel(A, m0, M, G::BM, P.rowb);
-    P.b = panel(B, n0, N, G::BN, P.rowb);
-    P.sa = panel(SA, m0, M, G::BM, P.kblocks);
-    P.sb = panel(SB, n0, N, G::BN, P.kblocks);
+    const int rowb = (int)(K / 2), kblocks = (int)(K / 32);
+    auto panels_of = [&](int64_t m0, int64_t n0) {
+        Panels P;
+        P.rowb = rowb;
+        P.kblocks = kblocks;
+        P.a = panel(A, m0, M, G::BM, rowb);
+        P.b = panel(B, n0, N, G::BN, rowb);
+        P.sa = panel(SA, m0, M, G::BM, kblocks);
+        P.sb = panel(SB, n0, N, G::BN, kblocks);
+        return P;
+    };
+    // A zero-size twin of the panels: stages past the end of K are "loaded"
+    // through it, which returns zeros without touching memory.  Every step
+    // then issues exactly one stage of DMA, the number of stages in flight is
+    // constant and every wait below is a constant.
+    Panels Z;
+    Z.rowb = rowb;
+    Z.kblocks = kblocks;
+    Z.a = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, 0x00020000);
+    Z.b = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, 0, 0x00020000);
+    Z.sa = __builtin_amdgcn_make_buffer_rsrc((void*)SA, (short)0, 0, 0x00020000);
+    Z.sb = __builtin_amdgcn_make_buffer_rsrc((void*)SB, (short)0, 0, 0x00020000);
+    // the first D - 1 stages of a tile: scale group 0 goes first, ahead of the
+    // codes of stage 0, so waiting for a stage's codes also covers its scales
+    // (vector memory completes in order)
+    auto prologue = [&](const Panels& P) {
+        scale_dma<G>(sgb, P.sa, P.sb, P.kblocks, 0, wave, lane);
+#pragma unroll
+        for (int p = 0; p < D - 1; p++) {
+            const DmaSlot d = {smem + p * G::STAGE, p < nst ? P : Z, p, wave, lane};
+            stage_dma<G>(d);
+        }
+    };
+    // EXACT (bf16 C, ldc and N multiples of 8): stores of whole 16-byte
+    // chunks, an exact count per wave
+    static_assert(!EXACT || CBF16, "the exact store path writes bf16");
+    constexpr bool exact = EXACT;
+
+    int lin = blockIdx.x;
+    int64_t m0, n0;
+    tile_of(lin, m0, n0);
+    Panels P = panels_of(m0, n0);
 
     v16f acc[TI][TJ];
 #pragma unroll
@@ -408,24 +516,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // A zero-size twin of the panels: stages past the end of K are "loaded"
-    // through it, which returns zeros without touching memory.  Every step
-    // then issues exactly one stage of DMA, the number of stages in flight is
-    // constant and every wait below is a constant.
-    Panels Z = P;
-    Z.a = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, 0x00020000);
-    Z.b = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, 0, 0x00020000);
-    Z.sa = __builtin_amdgcn_make_buffer_rsrc((void*)SA, (short)0, 0, 0x00020000);
-    Z.sb = __builtin_amdgcn_make_buffer_rsrc((void*)SB, (short)0, 0, 0x00020000);
-
-    // scale group 0 goes first, ahead of the codes of stage 0, so waiting for
-    // a stage's codes also covers its scales (vector memory completes in order)
-    scale_dma<G>(sgb, P.sa, P.sb, P.kblocks, 0, wave, lane);
-#pragma unroll
-    for (int p = 0; p < D - 1; p++) {
-        const DmaSlot d = {smem + p * G::STAGE, p < nst ? P : Z, p, wave, lane};
-        stage_dma<G>(d);
-    }
+    prologue(P);
     wait_vm<(D - 2) * L>();                          // stage 0 and scale group 0 have landed
     bar();
     // two operand sets in ping-pong: X holds even substeps, Y odd ones; the
@@ -434,87 +525,91 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
     Scl<G> S;
     Cur<G> Q;
     load_ops<G>(X, smem, 0, ra, rb, half);
-    for (int s = 0; s < nst; s++) {
-        const uint8_t* st = smem + (s % D) * G::STAGE;
-        if ((s & 3) == 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
-        pick<G>(Q, S, s & 3);
-        // substep 0 of stage s, the reads of substep 1 and the DMA of stage
-        // s + D - 1 into the buffer of stage s - 1 (every wave finished its
-        // reads of it before the previous barrier).  A stage that opens a
-        // scale group is preceded by that group's DMA into the buffer the
-        // group before last used, long since read.
-        const int nx = s + D - 1;
-        if (nx % SG == 0)
-            scale_dma<G>(sgb + ((nx / SG) & 1) * G::SBUF, nx < nst ? P.sa : Z.sa, nx < nst ? P.sb : Z.sb, P.kblocks,
-                         nx / SG, wave, lane);
-        const DmaSlot d = {smem + (nx % D) * G::STAGE, nx < nst ? P : Z, nx, wave, lane};
-        substep<G, 0, L>(X, Q, acc, Y, st, 1, ra, rb, half, &d);
-        // stage s + 1 (and its scales) must have landed before its first
-        // operands are read; what may stay in flight is the DMA of the later
-        // stages, plus one scale group if one of them opens a group (after the
-        // last stage the read is of a buffer that is never used)
-        bool extra = false;
+    bool pend = false;       // the previous tile's C stores are in flight, issued after this tile's first stages
+    for (;;) {
+        for (int s = 0; s < nst; s++) {
+            const uint8_t* st = smem + (s % D) * G::STAGE;
+            if ((s & 3) == 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
+            pick<G>(Q, S, s & 3);
+            // substep 0 of stage s, the reads of substep 1 and the DMA of
+            // stage s + D - 1 into the buffer of stage s - 1 (every wave
+            // finished its reads of it before the previous barrier).  A stage
+            // that opens a scale group is preceded by that group's DMA into
+            // the buffer the group before last used, long since read.
+            const int nx = s + D - 1;
+            if (nx % SG == 0)
+                scale_dma<G>(sgb + ((nx / SG) & 1) * G::SBUF, nx < nst ? P.sa : Z.sa, nx < nst ? P.sb : Z.sb,
+                             P.kblocks, nx / SG, wave, lane);
+            const DmaSlot d = {smem + (nx % D) * G::STAGE, nx < nst ? P : Z, nx, wave, lane};
+            substep<G, 0, L>(X, Q, acc, Y, st, 1, ra, rb, half, &d);
+            // stage s + 1 (and its scales) must have landed before its first
+            // operands are read.  What may stay in flight: the DMA of the
+            // later stages, one scale group if one of them opens a group, and
+            // the previous tile's C stores while they are younger than stage
+            // s + 1 (after the last stage the read is of a buffer never used).
+            bool extra = false;
 #pragma unroll
-        for (int q = 2; q <= D - 1; q++) extra = extra || ((s + q) % SG == 0);
-        if (extra) wait_vm<(D - 2) * L + G::PWS>();
-        else wait_vm<(D - 2) * L>();
-        bar();
-        handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
-    }
-    wait_vm<0>();
-
-    if constexpr (CBF16) {
-        // each wave stages one 32-row strip of its tile at a time as bf16 rows
-        // in a private LDS area, then writes C with 16-byte stores (a row
-        // segment of a wave-store is contiguous).  LDS operations of one wave
-        // complete in order, so the strips need no barrier between them.
-        __syncthreads();
-        uint8_t* ct = smem + wave * 32 * CROW;
-        constexpr int CPRC = 4 * TJ;                 // 16-byte chunks per strip row
-        constexpr int RPI = 64 / CPRC;               // strip rows per wave-store
-        const bool vec = (ldc % 8) == 0;
-#pragma unroll
-        for (int i = 0; i < TI; i++) {
-#pragma unroll
-            for (int j = 0; j < TJ; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    typedef float f2 __attribute__((ext_vector_type(2)));
-                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-                    const f2 f = {acc[i][j][r], acc[i][j][r + 1]};
-                    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2));
-                    const int ml = 8 * (r / 4) + 4 * half + (r % 4), nl = j * 32 + lrow;
-                    *reinterpret_cast<uint16_t*>(ct + ml * CROW + nl * 2) = (uint16_t)w;
-                    *reinterpret_cast<uint16_t*>(ct + (ml + 1) * CROW + nl * 2) = (uint16_t)(w >> 16);
-                }
-#pragma unroll
-            for (int q = 0; q < 32 / RPI; q++) {
-                const int row = q * RPI + lane / CPRC, chunk = lane % CPRC;
-                const int64_t m = m0 + wm * 32 * TI + i * 32 + row, n = n0 + wn * 32 * TJ + chunk * 8;
-                const u32x4v v = *reinterpret_cast<const u32x4v*>(ct + row * CROW + chunk * 16);
-                if (m >= M || n >= N) continue;
-                uint16_t* dst = static_cast<uint16_t*>(C) + m * ldc + n;
-                if (vec && n + 8 <= N) {
-                    *reinterpret_cast<u32x4v*>(dst) = v;
-                } else {
-                    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
-                    for (int k = 0; k < 8 && n + k < N; k++) dst[k] = (uint16_t)(e[k >> 1] >> (16 * (k & 1)));
-                }
-            }
+            for (int q = 2; q <= D - 1; q++) extra = extra || ((s + q) % SG == 0);
+            if (pend && s < D - 2) wait_vm<(D - 2) * L + NSTORE>();
+            else if (extra) wait_vm<(D - 2) * L + G::PWS>();
+            else wait_vm<(D - 2) * L>();
+            bar();
+            handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
         }
-    } else {
+        wait_vm<0>();        // this tile's DMA, including the zero-size loads past K
+        bar();               // every wave is done with the ring and the scale buffers
+
+        const int nlin = lin + (int)gridDim.x;
+        const bool more = nlin < T;
+        int64_t nm0 = 0, nn0 = 0;
+        Panels NP = P;
+        if (more) {
+            tile_of(nlin, nm0, nn0);
+            NP = panels_of(nm0, nn0);
+        }
+        if constexpr (exact) {
+            // the next tile's first stages go out first; the stores follow and
+            // drain while that tile starts
+            if (more) prologue(NP);
+            store_c_bf16<G, true>(acc, ct, C, m0, n0, M, N, ldc, wm, wn, lane, half, lrow);
+        } else {
+            if constexpr (CBF16) {
+                store_c_bf16<G, false>(acc, ct, C, m0, n0, M, N, ldc, wm, wn, lane, half, lrow);
+            } else {
+#pragma unroll
+                for (int i = 0; i < TI; i++)
+#pragma unroll
+                    for (int j = 0; j < TJ; j++) {
+                        const int64_t n = n0 + wn * 32 * TJ + j * 32 + lrow;
+                        if (n >= N) continue;
+#pragma unroll
+                        for (int r = 0; r < 16; r++) {
+                            const int64_t m = m0 + wm * 32 * TI + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                            if (m < M) static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
+                        }
+                    }
+            }
+            wait_vm<0>();
+            if (more) prologue(NP);
+        }
+        if (!more) break;
 #pragma unroll
         for (int i = 0; i < TI; i++)
 #pragma unroll
-            for (int j = 0; j < TJ; j++) {
-                const int64_t n = n0 + wn * 32 * TJ + j * 32 + lrow;
-                if (n >= N) continue;
+            for (int j = 0; j < TJ; j++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int64_t m = m0 + wm * 32 * TI + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                    if (m < M) static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
-                }
-            }
+                for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+        // the next tile's stage 0 and scale group 0 must have landed; its
+        // stages 1 .. D-2 and, on the exact path, the C stores may stay in flight
+        if constexpr (exact) wait_vm<(D - 2) * L + NSTORE>();
+        else wait_vm<(D - 2) * L>();
+        bar();               // also: every wave's strip reads are done before stage D-1's DMA refills that slot
+        load_ops<G>(X, smem, 0, ra, rb, half);
+        lin = nlin;
+        m0 = nm0;
+        n0 = nn0;
+        P = NP;
+        pend = exact;
     }
 }
 
@@ -534,8 +629,25 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     if (K % 1024 == 0) {
         using G = GemmGeo;
         const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
-        if (c_bf16) k_gemm_tiled<true, G, GEMM_D><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
-        else k_gemm_tiled<false, G, GEMM_D><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+        // persistent: one workgroup per CU (the LDS ring fills a CU), each
+        // looping over its tiles
+        static int cus = 0;
+        if (cus == 0) {
+            int dev = 0, c = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+                cus = c;
+            else
+                cus = 256;
+        }
+        const int64_t grid = tiles < cus ? tiles : cus;
+        const bool exact = c_bf16 && ldc % 8 == 0 && N % 8 == 0 && (int64_t)G::BM * ldc * 2 < 0x80000000LL;
+        if (exact)
+            k_gemm_tiled<true, true, G, GEMM_D><<<(unsigned)grid, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+        else if (c_bf16)
+            k_gemm_tiled<true, false, G, GEMM_D><<<(unsigned)grid, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+        else
+            k_gemm_tiled<false, false, G, GEMM_D><<<(unsigned)grid, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));

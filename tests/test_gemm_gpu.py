@@ -42,7 +42,8 @@ def bf16_of(x64):
 
 @pytest.mark.parametrize("M,N,K", [(200, 136, 512), (128, 128, 128), (1, 1, 256), (257, 300, 384),
                                    (70, 90, 32), (130, 40, 96), (33, 300, 160), (256, 256, 224),
-                                   (257, 300, 1024), (200, 520, 2048), (300, 257, 3072), (512, 256, 1024)])
+                                   (257, 300, 1024), (200, 520, 2048), (300, 257, 3072), (512, 256, 1024),
+                                   (2304, 8200, 1024), (2304, 8204, 1024)])
 def test_exact_case_bit_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     ca = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
