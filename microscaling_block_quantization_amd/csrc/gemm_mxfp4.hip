@@ -241,25 +241,42 @@ struct Ops {
     u32x4v a[G::TI], b[G::TJ];
 };
 
-// the scale dwords of this lane's rows for 4 consecutive stages (one 16-byte
-// unit per row tile, A's then B's), read once per 4 stages and shifted by
-// 8*half: then byte 0 is this lane's block of the stage's first substep and
-// byte 2 that of its second (the op_sel values 0 and 2)
+// the scale bytes of this lane's rows for 4 consecutive stages, read once per
+// 4 stages from one 16-byte unit per row tile (4 stages x 4 blocks) and packed
+// by a byte permute into two dwords per row tile: p[2c] holds stages 2c and
+// 2c+1 as [b(2c, h), b(2c+1, h), b(2c, 2+h), b(2c+1, 2+h)], where b(q, k) is
+// block k of stage q and h this lane's half.  Shifted right by 8*(s&1), byte
+// 0 is the block of the stage's first substep and byte 2 that of its second
+// (the op_sel values 0 and 2).
 template <class G>
 struct Scl {
-    u32x4v q[G::TI + G::TJ];
+    uint32_t p[G::TI + G::TJ][2];
 };
 
 template <class G>
 __device__ __forceinline__ void load_scl(Scl<G>& o, const uint8_t* __restrict__ buf, int hf, int ra, int rb,
                                          int half) {
+    const uint32_t sel = half ? 0x07030501u : 0x06020400u;
 #pragma unroll
-    for (int i = 0; i < G::TI; i++)
-        o.q[i] = *reinterpret_cast<const u32x4v*>(buf + (hf * G::BM + ra + 32 * i) * 16) >> (8u * half);
+    for (int i = 0; i < G::TI + G::TJ; i++) {
+        const int off = i < G::TI ? (hf * G::BM + ra + 32 * i) * 16
+                                  : G::BM * G::SROW + (hf * G::BN + rb + 32 * (i - G::TI)) * 16;
+        const u32x4v q = *reinterpret_cast<const u32x4v*>(buf + off);
+        o.p[i][0] = __builtin_amdgcn_perm(q.y, q.x, sel);
+        o.p[i][1] = __builtin_amdgcn_perm(q.w, q.z, sel);
+    }
+}
+
+// this stage's scale operands
+template <class G>
+struct Cur {
+    int x[G::TI + G::TJ];
+};
+
+template <class G>
+__device__ __forceinline__ void pick(Cur<G>& c, const Scl<G>& sc, int u) {
 #pragma unroll
-    for (int j = 0; j < G::TJ; j++)
-        o.q[G::TI + j] =
-            *reinterpret_cast<const u32x4v*>(buf + G::BM * G::SROW + (hf * G::BN + rb + 32 * j) * 16) >> (8u * half);
+    for (int i = 0; i < G::TI + G::TJ; i++) c.x[i] = (int)((u & 2 ? sc.p[i][1] : sc.p[i][0]) >> (8 * (u & 1)));
 }
 
 // LDS read k (0 .. NOPS-1) of the operands of substep t: A fragments, B
@@ -290,21 +307,6 @@ __device__ __forceinline__ void load_ops(Ops<G>& o, const uint8_t* __restrict__ 
 // texture unit for a while and the MFMA in flight hides it; every LDS read
 // has the rest of the substep to land.  After the shift by 8*half this lane's
 // scale byte (block 2t + half of the stage) is byte 2*(t&1): the op_sel value.
-// this stage's scale dwords: component s % 4 of the registers of Scl
-template <class G>
-struct Cur {
-    int x[G::TI + G::TJ];
-};
-
-template <class G>
-__device__ __forceinline__ void pick(Cur<G>& c, const Scl<G>& sc, int u) {
-#pragma unroll
-    for (int i = 0; i < G::TI + G::TJ; i++) {
-        const u32x4v q = sc.q[i];
-        c.x[i] = (int)(u == 0 ? q.x : u == 1 ? q.y : u == 2 ? q.z : q.w);
-    }
-}
-
 template <class G, int T1, int NV>
 __device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16f (&acc)[G::TI][G::TJ], Ops<G>& nxt,
                                         const uint8_t* __restrict__ st, int t, int ra, int rb, int half,
@@ -525,11 +527,11 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
     Scl<G> S;
     Cur<G> Q;
     load_ops<G>(X, smem, 0, ra, rb, half);
+    load_scl<G>(S, sgb, 0, ra, rb, half);
     bool pend = false;       // the previous tile's C stores are in flight, issued after this tile's first stages
     for (;;) {
         for (int s = 0; s < nst; s++) {
             const uint8_t* st = smem + (s % D) * G::STAGE;
-            if ((s & 3) == 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
             pick<G>(Q, S, s & 3);
             // substep 0 of stage s, the reads of substep 1 and the DMA of
             // stage s + D - 1 into the buffer of stage s - 1 (every wave
@@ -554,6 +556,10 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
             else if (extra) wait_vm<(D - 2) * L + G::PWS>();
             else wait_vm<(D - 2) * L>();
             bar();
+            // the scales of stages s + 1 .. s + 4 have landed with stage s + 1:
+            // read them now, under the MFMAs of the handover
+            if (((s + 1) & 3) == 0 && s + 1 < nst)
+                load_scl<G>(S, sgb + (((s + 1) / SG) & 1) * G::SBUF, ((s + 1) % SG) / 4, ra, rb, half);
             handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
         }
         wait_vm<0>();        // this tile's DMA, including the zero-size loads past K
@@ -605,6 +611,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
         else wait_vm<(D - 2) * L>();
         bar();               // also: every wave's strip reads are done before stage D-1's DMA refills that slot
         load_ops<G>(X, smem, 0, ra, rb, half);
+        load_scl<G>(S, sgb, 0, ra, rb, half);
         lin = nlin;
         m0 = nm0;
         n0 = nn0;
