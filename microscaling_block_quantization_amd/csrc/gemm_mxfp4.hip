@@ -532,6 +532,8 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
     for (;;) {
         for (int s = 0; s < nst; s++) {
             const uint8_t* st = smem + (s % D) * G::STAGE;
+            // stages 0 .. 3 of a tile were read after its first stage landed
+            if ((s & 3) == 0 && s > 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
             pick<G>(Q, S, s & 3);
             // substep 0 of stage s, the reads of substep 1 and the DMA of
             // stage s + D - 1 into the buffer of stage s - 1 (every wave
@@ -556,10 +558,6 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
             else if (extra) wait_vm<(D - 2) * L + G::PWS>();
             else wait_vm<(D - 2) * L>();
             bar();
-            // the scales of stages s + 1 .. s + 4 have landed with stage s + 1:
-            // read them now, under the MFMAs of the handover
-            if (((s + 1) & 3) == 0 && s + 1 < nst)
-                load_scl<G>(S, sgb + (((s + 1) / SG) & 1) * G::SBUF, ((s + 1) % SG) / 4, ra, rb, half);
             handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
         }
         wait_vm<0>();        // this tile's DMA, including the zero-size loads past K
