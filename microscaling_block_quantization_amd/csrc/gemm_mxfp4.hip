@@ -323,6 +323,13 @@ __device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16
         const int i = k / G::TJ, j = k % G::TJ;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op8(cur.a[i]), op8(cur.b[j]), acc[i][j], 4, 4,
                                                                    2 * T1, xa[i], 2 * T1, xb[j]);
+        // An empty volatile statement that names the result: it emits nothing,
+        // but it keeps the MFMA ahead of the fence below.  (The result is only
+        // used by the next stage, so the instruction selector would otherwise
+        // place every MFMA of the substep after the last fence.)
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" ::"v"(acc[i][j]));
+#endif
 #pragma unroll
         for (int q = k * G::NOPS / NM; q < (k + 1) * G::NOPS / NM; q++) ops_piece<G>(nxt, st, t, ra, rb, half, q);
 #pragma unroll
@@ -335,6 +342,26 @@ __device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// the same with N0, N1 or N2 chosen by a uniform sel (0, 1, 2).  One asm
+// statement: a branch in the source would split the basic block, and the
+// compiler then sinks the preceding MFMAs below the wait.
+template <int N0, int N1, int N2>
+__device__ __forceinline__ void wait_vm_sel(int sel) {
+    asm volatile(
+        "s_cmp_eq_u32 %0, 0\n\t"
+        "s_cbranch_scc1 1f\n\t"
+        "s_cmp_eq_u32 %0, 1\n\t"
+        "s_cbranch_scc1 2f\n\t"
+        "s_waitcnt vmcnt(%3)\n\t"
+        "s_branch 3f\n"
+        "1:\n\t"
+        "s_waitcnt vmcnt(%1)\n\t"
+        "s_branch 3f\n"
+        "2:\n\t"
+        "s_waitcnt vmcnt(%2)\n"
+        "3:" ::"s"(sel), "n"(N0), "n"(N1), "n"(N2) : "memory", "scc");
 }
 
 // all waves' DMA of a stage has landed (each wave waited for its own) and
@@ -554,9 +581,9 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
             bool extra = false;
 #pragma unroll
             for (int q = 2; q <= D - 1; q++) extra = extra || ((s + q) % SG == 0);
-            if (pend && s < D - 2) wait_vm<(D - 2) * L + NSTORE>();
-            else if (extra) wait_vm<(D - 2) * L + G::PWS>();
-            else wait_vm<(D - 2) * L>();
+            const int sel = (pend && s < D - 2) ? 2 : (extra ? 1 : 0);
+            wait_vm_sel<(D - 2) * L, (D - 2) * L + G::PWS, (D - 2) * L + NSTORE>(
+                __builtin_amdgcn_readfirstlane(sel));
             bar();
             handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
         }
