@@ -307,7 +307,7 @@ __device__ __forceinline__ void load_ops(Ops<G>& o, const uint8_t* __restrict__ 
 // texture unit for a while and the MFMA in flight hides it; every LDS read
 // has the rest of the substep to land.  After the shift by 8*half this lane's
 // scale byte (block 2t + half of the stage) is byte 2*(t&1): the op_sel value.
-template <class G, int T1, int NV>
+template <class G, int T1, int NV, int NOFF>
 __device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16f (&acc)[G::TI][G::TJ], Ops<G>& nxt,
                                         const uint8_t* __restrict__ st, int t, int ra, int rb, int half,
                                         const DmaSlot* d) {
@@ -333,7 +333,7 @@ __device__ __forceinline__ void substep(const Ops<G>& cur, const Cur<G>& sc, v16
 #pragma unroll
         for (int q = k * G::NOPS / NM; q < (k + 1) * G::NOPS / NM; q++) ops_piece<G>(nxt, st, t, ra, rb, half, q);
 #pragma unroll
-        for (int q = k * NV / NM; q < (k + 1) * NV / NM; q++) dma_piece<G>(*d, q);
+        for (int q = k * NV / NM; q < (k + 1) * NV / NM; q++) dma_piece<G>(*d, NOFF + q);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -375,13 +375,15 @@ __device__ __forceinline__ void bar() {
 }
 
 // the stage handover: the last substep of the current stage multiplies while
-// the first operands of the next stage are read from `nxt`.  The buffers are
-// distinct restrict-qualified objects here, so the operand reads carry no
-// dependence on the DMA in flight.
-template <class G, int T1>
+// the first operands of the next stage are read from `nxt` and the first
+// pieces of a later stage's DMA go out (into the slot of the stage just
+// finished).  The buffers are distinct restrict-qualified objects here, so
+// the operand reads carry no dependence on the DMA in flight.
+template <class G, int T1, int NV>
 __device__ __forceinline__ void handover(const uint8_t* __restrict__ nxt, const Ops<G>& cur, const Cur<G>& sc,
-                                         v16f (&acc)[G::TI][G::TJ], Ops<G>& o, int ra, int rb, int half) {
-    substep<G, T1, 0>(cur, sc, acc, o, nxt, 0, ra, rb, half, nullptr);
+                                         v16f (&acc)[G::TI][G::TJ], Ops<G>& o, int ra, int rb, int half,
+                                         const DmaSlot* d) {
+    substep<G, T1, NV, 0>(cur, sc, acc, o, nxt, 0, ra, rb, half, d);
 }
 
 // one C tile's store path: bf16 rows staged per 16-row strip in a private
@@ -545,9 +547,23 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
+    // a stage's DMA goes out in two parts: pieces [0, L1) in the handover
+    // after the barrier that frees its slot, the rest in the next substep
+    constexpr int L1 = L / 2;
+    // the first part of stage D - 1 (and its scale group, if it opens one),
+    // once the barrier has freed its slot
+    auto first_part = [&](const Panels& P_, int st_) {
+        if (st_ % SG == 0)
+            scale_dma<G>(sgb + ((st_ / SG) & 1) * G::SBUF, st_ < nst ? P_.sa : Z.sa, st_ < nst ? P_.sb : Z.sb,
+                         P_.kblocks, st_ / SG, wave, lane);
+        const DmaSlot d = {smem + (st_ % D) * G::STAGE, st_ < nst ? P_ : Z, st_, wave, lane};
+#pragma unroll
+        for (int q = 0; q < L1; q++) dma_piece<G>(d, q);
+    };
     prologue(P);
     wait_vm<(D - 2) * L>();                          // stage 0 and scale group 0 have landed
     bar();
+    first_part(P, D - 1);
     // two operand sets in ping-pong: X holds even substeps, Y odd ones; the
     // scale registers hold 4 stages and are refilled at every 4th stage
     Ops<G> X, Y;
@@ -562,17 +578,12 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
             // stages 0 .. 3 of a tile were read after its first stage landed
             if ((s & 3) == 0 && s > 0) load_scl<G>(S, sgb + ((s / SG) & 1) * G::SBUF, (s % SG) / 4, ra, rb, half);
             pick<G>(Q, S, s & 3);
-            // substep 0 of stage s, the reads of substep 1 and the DMA of
-            // stage s + D - 1 into the buffer of stage s - 1 (every wave
-            // finished its reads of it before the previous barrier).  A stage
-            // that opens a scale group is preceded by that group's DMA into
-            // the buffer the group before last used, long since read.
+            // substep 0 of stage s, the reads of substep 1 and the rest of the
+            // DMA of stage s + D - 1 (its first part went out in the handover
+            // before, after the barrier that freed its slot)
             const int nx = s + D - 1;
-            if (nx % SG == 0)
-                scale_dma<G>(sgb + ((nx / SG) & 1) * G::SBUF, nx < nst ? P.sa : Z.sa, nx < nst ? P.sb : Z.sb,
-                             P.kblocks, nx / SG, wave, lane);
             const DmaSlot d = {smem + (nx % D) * G::STAGE, nx < nst ? P : Z, nx, wave, lane};
-            substep<G, 0, L>(X, Q, acc, Y, st, 1, ra, rb, half, &d);
+            substep<G, 0, L - L1, L1>(X, Q, acc, Y, st, 1, ra, rb, half, &d);
             // stage s + 1 (and its scales) must have landed before its first
             // operands are read.  What may stay in flight: the DMA of the
             // later stages, one scale group if one of them opens a group, and
@@ -585,7 +596,14 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
             wait_vm_sel<(D - 2) * L, (D - 2) * L + G::PWS, (D - 2) * L + NSTORE>(
                 __builtin_amdgcn_readfirstlane(sel));
             bar();
-            handover<G, 1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half);
+            // slot s % D is free now: the first part of stage s + D goes out
+            // under the handover's MFMAs, after its scale group if it opens one
+            const int nn = s + D;
+            if (nn % SG == 0)
+                scale_dma<G>(sgb + ((nn / SG) & 1) * G::SBUF, nn < nst ? P.sa : Z.sa, nn < nst ? P.sb : Z.sb,
+                             P.kblocks, nn / SG, wave, lane);
+            const DmaSlot d2 = {smem + (nn % D) * G::STAGE, nn < nst ? P : Z, nn, wave, lane};
+            handover<G, 1, L1>(smem + ((s + 1) % D) * G::STAGE, Y, Q, acc, X, ra, rb, half, &d2);
         }
         wait_vm<0>();        // this tile's DMA, including the zero-size loads past K
         bar();               // every wave is done with the ring and the scale buffers
@@ -635,6 +653,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
         if constexpr (exact) wait_vm<(D - 2) * L + NSTORE>();
         else wait_vm<(D - 2) * L>();
         bar();               // also: every wave's strip reads are done before stage D-1's DMA refills that slot
+        first_part(NP, D - 1);
         load_ops<G>(X, smem, 0, ra, rb, half);
         load_scl<G>(S, sgb, 0, ra, rb, half);
         lin = nlin;
