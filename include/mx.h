@@ -185,12 +185,15 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
             void *stream);
 
 /* Block-scaled GEMM ([U] Sec. 3 Fig. 4, Sec. 4 Fig. 5): C = deq(A) . deq(B)^T
- * with A an M x K and B an N x K quantized tensor, both MXFP4 (E2M1 elements,
- * E8M0 scales, 1 x 32 row blocks along K, any E8M0 rule), fp32 accumulation,
- * C (M x N, row stride ldc elements) in bf16 (rounded to nearest even) or
- * fp32.  Runs on the gfx950 block-scaled FP4 matrix instructions.  Shapes:
- * K % 32 == 0, as the 1 x 32 blocks require (MX_ERR_ARG otherwise); K a
- * multiple of 1024 takes the LDS-staged kernel, other multiples of 32 a
+ * with A an M x K and B an N x K quantized tensor, each with E8M0 scales on
+ * 1 x 32 row blocks along K (any E8M0 rule) and E2M1 (MXFP4) or FP6 E2M3 /
+ * E3M2 (MXFP6) elements, the two operands' element types chosen
+ * independently (the mixed 4-/6-bit products of [A], main results); fp32
+ * accumulation, C (M x N, row stride ldc elements) in bf16 (rounded to nearest
+ * even) or fp32.  Runs on the gfx950 block-scaled FP8/FP6/FP4 matrix
+ * instructions.  Other formats: MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0, as
+ * the 1 x 32 blocks require (MX_ERR_ARG otherwise); MXFP4 x MXFP4 with K a
+ * multiple of 1024 takes the LDS-staged kernel, every other case a
  * register-only one; any M, N.                                              */
 int mx_gemm(const mx_format *fa, const mx_qtensor *a, const mx_format *fb,
             const mx_qtensor *b, void *c, int64_t ldc, int c_dtype, void *stream);

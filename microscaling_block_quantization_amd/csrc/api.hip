@@ -270,7 +270,7 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
             int64_t ldc, int c_dtype, void* stream) {
     if (!fa || !fb || !a || !b) return MX_ERR_ARG;
     for (const mx_format* f : {fa, fb}) {
-        if (f->elem != MX_ELEM_E2M1 || f->scale != MX_SCALE_E8M0 || f->block_rows != 1 ||
+        if (!mxk::gemm_elem_ok(f->elem) || f->scale != MX_SCALE_E8M0 || f->block_rows != 1 ||
             f->block_cols != 32 || f->asymmetric || f->hadamard || f->macro_cols)
             return MX_ERR_UNSUPPORTED;
     }
@@ -289,7 +289,8 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     if (!aligned16(c) || !aligned16(a->codes) || !aligned16(b->codes) || !aligned16(a->scales) ||
         !aligned16(b->scales))
         return MX_ERR_ALIGN;
-    return hip_status(mxk::launch_gemm(static_cast<const uint8_t*>(a->codes), static_cast<const uint8_t*>(a->scales),
+    return hip_status(mxk::launch_gemm(fa->elem, static_cast<const uint8_t*>(a->codes),
+                                       static_cast<const uint8_t*>(a->scales), fb->elem,
                                        static_cast<const uint8_t*>(b->codes), static_cast<const uint8_t*>(b->scales),
                                        c, M, N, K, ldc, c_dtype == MX_DTYPE_BF16, static_cast<hipStream_t>(stream)));
 }

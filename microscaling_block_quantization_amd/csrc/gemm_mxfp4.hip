@@ -29,14 +29,43 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int TM = 128, TN = 128, TK = 128;
 
-__device__ __forceinline__ v8i as_operand(uint4 w) {
+// Element formats of the matrix instruction's type fields (CBSZ for A, BLGP for
+// B): FP6 E2M3, FP6 E3M2, FP4 E2M1.  The library's own element enumeration
+// differs; fmt_of() maps it.
+constexpr int MF_E2M3 = 2, MF_E3M2 = 3, MF_E2M1 = 4;
+constexpr int fmt_of(int elem) { return elem == E2M1 ? MF_E2M1 : elem == E2M3 ? MF_E2M3 : MF_E3M2; }
+// bytes of one 32-element block: 16 for E2M1, 24 for FP6
+constexpr int block_bytes(int mf) { return mf == MF_E2M1 ? 16 : 24; }
+
+// one lane's operand: the 32 codes of one block as the format packs them (two
+// E2M1 codes per byte, low nibble first; FP6 as a 6-bit stream from the low
+// bit of the first byte), which is the instruction's operand layout for that
+// type: four registers for E2M1, six for FP6.  p is 8-byte aligned.
+template <int MF>
+__device__ __forceinline__ v8i load_block(const uint8_t* p) {
     v8i v;
-    v[0] = (int)w.x; v[1] = (int)w.y; v[2] = (int)w.z; v[3] = (int)w.w;
-    v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0;
+    if constexpr (MF == MF_E2M1) {
+        const uint4 w = *reinterpret_cast<const uint4*>(p);
+        v[0] = (int)w.x; v[1] = (int)w.y; v[2] = (int)w.z; v[3] = (int)w.w;
+    } else {
+        const uint2* q = reinterpret_cast<const uint2*>(p);
+        const uint2 w0 = q[0], w1 = q[1], w2 = q[2];
+        v[0] = (int)w0.x; v[1] = (int)w0.y; v[2] = (int)w1.x; v[3] = (int)w1.y; v[4] = (int)w2.x; v[5] = (int)w2.y;
+    }
+    return v;
+}
+__device__ __forceinline__ v8i zero_block() {
+    v8i v;
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0;
     return v;
 }
 
-template <bool CBF16>
+// Register-only kernel, any element pair: 4 waves of 64 x 64 outputs (2 x 2
+// MFMA tiles), operands straight from global memory.
+template <bool CBF16, int FA, int FB>
 __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
                                                      void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc) {
@@ -44,7 +73,8 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
     const int half = lane >> 5, row = lane & 31;
     const int64_t m0 = (int64_t)blockIdx.y * TM + (wave >> 1) * 64;
     const int64_t n0 = (int64_t)blockIdx.x * TN + (wave & 1) * 64;
-    const int64_t rowb = K / 2, kblocks = K / 32;
+    const int64_t kblocks = K / 32;
+    const int64_t rowa = kblocks * block_bytes(FA), rowb = kblocks * block_bytes(FB);
 
     int64_t ra[2], rb[2];
 #pragma unroll
@@ -64,7 +94,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
     // K advances 128 per step; a 32-element block past the end of K (K is a
     // multiple of 32 only) contributes zero codes under scale code 0
     for (int64_t k0 = 0; k0 < K; k0 += TK) {
-        uint4 av[2][2], bv[2][2];
+        v8i av[2][2], bv[2][2];
         int sa[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -73,8 +103,8 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
             for (int kk = 0; kk < 2; kk++) {
                 const int64_t kb = k0 / 32 + 2 * kk + half;   // this lane's K block
                 const bool in = kb < kblocks;
-                av[i][kk] = in ? *reinterpret_cast<const uint4*>(A + ra[i] * rowb + kb * 16) : make_uint4(0, 0, 0, 0);
-                bv[i][kk] = in ? *reinterpret_cast<const uint4*>(B + rb[i] * rowb + kb * 16) : make_uint4(0, 0, 0, 0);
+                av[i][kk] = in ? load_block<FA>(A + ra[i] * rowa + kb * block_bytes(FA)) : zero_block();
+                bv[i][kk] = in ? load_block<FB>(B + rb[i] * rowb + kb * block_bytes(FB)) : zero_block();
                 ca[kk] = in ? SA[ra[i] * kblocks + kb] : 0u;
                 cb[kk] = in ? SB[rb[i] * kblocks + kb] : 0u;
             }
@@ -87,9 +117,9 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    as_operand(av[i][0]), as_operand(bv[j][0]), acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
+                    av[i][0], bv[j][0], acc[i][j], FA, FB, 0, sa[i], 0, sb[j]);
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    as_operand(av[i][1]), as_operand(bv[j][1]), acc[i][j], 4, 4, 2, sa[i], 2, sb[j]);
+                    av[i][1], bv[j][1], acc[i][j], FA, FB, 2, sa[i], 2, sb[j]);
             }
     }
 
@@ -670,14 +700,36 @@ __global__ __launch_bounds__(64 * G::NW, 1) void k_gemm_tiled(const uint8_t* __r
 // 4 waves: 2 x 2 waves of 4 x 4 MFMA tiles; 8 waves: 2 x 4 waves of 4 x 2
 using GemmGeo = Geo<GEMM_BK, 2, GEMM_WAVES / 2, 4, GEMM_WAVES == 8 ? 2 : 4>;
 
+template <int FA, int FB>
+void launch_simple(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c,
+                   int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
+    if (c_bf16) k_gemm_simple<true, FA, FB><<<grid, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    else k_gemm_simple<false, FA, FB><<<grid, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+}
+
+template <int FA>
+void launch_simple_b(int eb, const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c,
+                     int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    switch (fmt_of(eb)) {
+    case MF_E2M1: launch_simple<FA, MF_E2M1>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E2M3: launch_simple<FA, MF_E2M3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    default: launch_simple<FA, MF_E3M2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c,
-                       int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+bool gemm_elem_ok(int elem) { return elem == E2M1 || elem == E2M3 || elem == E3M2; }
+
+hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
+                       void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    // the tiled kernel fetches scales in 32-byte row groups (8 stages of 128):
-    // with K a multiple of 1024 every scale row starts 32-byte aligned
-    if (K % 1024 == 0) {
+    if (!gemm_elem_ok(ea) || !gemm_elem_ok(eb)) return hipErrorInvalidValue;
+    // the tiled kernel (E2M1 operands) fetches scales in 32-byte row groups (8
+    // stages of 128): with K a multiple of 1024 every scale row starts 32-byte
+    // aligned
+    if (ea == E2M1 && eb == E2M1 && K % 1024 == 0) {
         using G = GemmGeo;
         const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
         // persistent: one workgroup per CU (the LDS ring fills a CU), each
@@ -701,9 +753,11 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
             k_gemm_tiled<false, false, G, GEMM_D><<<(unsigned)grid, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
         return hipGetLastError();
     }
-    dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
-    if (c_bf16) k_gemm_simple<true><<<grid, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
-    else k_gemm_simple<false><<<grid, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    switch (fmt_of(ea)) {
+    case MF_E2M1: launch_simple_b<MF_E2M1>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E2M3: launch_simple_b<MF_E2M3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    default: launch_simple_b<MF_E3M2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    }
     return hipGetLastError();
 }
 

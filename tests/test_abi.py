@@ -146,6 +146,19 @@ def test_gemm_rejects_before_launch():
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
     assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
+    # element types outside E2M1 / E2M3 / E3M2, and non-E8M0 scales, are not run
+    for e in (mx.ELEM_INT4, mx.ELEM_E3M0):
+        g = mx.Format(elem=e).c()
+        assert L.mx_gemm(ctypes.byref(g), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
+                         mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    nv = mx.Format(scale=mx.SCALE_UE5M3).c()
+    assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(nv), ctypes.byref(b), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    # FP6 operands pass validation (checked here with a misaligned C, so no launch)
+    for e in (mx.ELEM_FP6_E2M3, mx.ELEM_FP6_E3M2):
+        g = mx.Format(elem=e).c()
+        assert L.mx_gemm(ctypes.byref(g), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
+                         mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
 
 
 def test_qsnr_rejects_before_launch():
