@@ -191,10 +191,15 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  * independently (the mixed 4-/6-bit products of [A], main results); fp32
  * accumulation, C (M x N, row stride ldc elements) in bf16 (rounded to nearest
  * even) or fp32.  Runs on the gfx950 block-scaled FP8/FP6/FP4 matrix
- * instructions.  Other formats: MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0, as
- * the 1 x 32 blocks require (MX_ERR_ARG otherwise); MXFP4 x MXFP4 with K a
- * multiple of 1024 takes the LDS-staged kernel, every other case a
- * register-only one; any M, N.                                              */
+ * instructions.  MXFP4 operands may carry macro-block scales (macro_cols
+ * 128, [U] Sec. 4 MBS and Fig. 5: the partial product of each 128-wide K
+ * step is multiplied by the two rows' UE4M3 macro scales); those products run
+ * on the register-only kernel.  Other formats: MX_ERR_UNSUPPORTED (macro
+ * scales with FP6 elements included).  Shapes: K % 32 == 0, as
+ * the 1 x 32 blocks require (MX_ERR_ARG otherwise); MXFP4 x MXFP4 without
+ * macro scales and with K a multiple of 1024 takes the LDS-staged kernel,
+ * every other case a register-only one; any M, N.  macro_scales must be set
+ * when the format has macro_cols (MX_ERR_ARG).                                              */
 int mx_gemm(const mx_format *fa, const mx_qtensor *a, const mx_format *fb,
             const mx_qtensor *b, void *c, int64_t ldc, int c_dtype, void *stream);
 

@@ -271,9 +271,13 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     if (!fa || !fb || !a || !b) return MX_ERR_ARG;
     for (const mx_format* f : {fa, fb}) {
         if (!mxk::gemm_elem_ok(f->elem) || f->scale != MX_SCALE_E8M0 || f->block_rows != 1 ||
-            f->block_cols != 32 || f->asymmetric || f->hadamard || f->macro_cols)
+            f->block_cols != 32 || f->asymmetric || f->hadamard)
             return MX_ERR_UNSUPPORTED;
     }
+    // macro-block scales: MXFP4 operands only (the sub-blocks are the 1 x 32
+    // blocks the instruction scales)
+    const bool mbs = fa->macro_cols || fb->macro_cols;
+    if (mbs && (fa->elem != MX_ELEM_E2M1 || fb->elem != MX_ELEM_E2M1)) return MX_ERR_UNSUPPORTED;
     int rc = check_format(fa, a->rows, a->cols);
     if (rc) return rc;
     rc = check_format(fb, b->rows, b->cols);
@@ -286,13 +290,16 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     if (M == 0 || N == 0) return MX_OK;
     if (K == 0) return MX_ERR_UNSUPPORTED;
     if (!c || !a->codes || !a->scales || !b->codes || !b->scales) return MX_ERR_ARG;
+    if ((fa->macro_cols && !a->macro_scales) || (fb->macro_cols && !b->macro_scales)) return MX_ERR_ARG;
     if (!aligned16(c) || !aligned16(a->codes) || !aligned16(b->codes) || !aligned16(a->scales) ||
         !aligned16(b->scales))
         return MX_ERR_ALIGN;
     return hip_status(mxk::launch_gemm(fa->elem, static_cast<const uint8_t*>(a->codes),
                                        static_cast<const uint8_t*>(a->scales), fb->elem,
                                        static_cast<const uint8_t*>(b->codes), static_cast<const uint8_t*>(b->scales),
-                                       c, M, N, K, ldc, c_dtype == MX_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+                                       c, M, N, K, ldc, c_dtype == MX_DTYPE_BF16, static_cast<hipStream_t>(stream),
+                                       fa->macro_cols ? static_cast<const uint8_t*>(a->macro_scales) : nullptr,
+                                       fb->macro_cols ? static_cast<const uint8_t*>(b->macro_scales) : nullptr));
 }
 
 }  // extern "C"

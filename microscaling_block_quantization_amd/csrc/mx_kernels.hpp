@@ -59,6 +59,7 @@ hipError_t launch_qsnr(int bf16, const void* a, const void* b, int64_t n, mxd::S
 // block-scaled GEMM; element codes E2M1, E2M3 or E3M2 for either operand
 bool gemm_elem_ok(int elem);
 hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
-                       void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s);
+                       void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
+                       const uint8_t* ma = nullptr, const uint8_t* mb = nullptr);
 
 }  // namespace mxk

@@ -154,6 +154,16 @@ def test_gemm_rejects_before_launch():
     nv = mx.Format(scale=mx.SCALE_UE5M3).c()
     assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(nv), ctypes.byref(b), 0x10000, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    # macro-block scales: MXFP4 only, and the macro_scales buffer is required
+    g6m = mx.Format(elem=mx.ELEM_FP6_E2M3, macro_cols=128).c()
+    assert L.mx_gemm(ctypes.byref(g6m), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    fm = mx.Format(macro_cols=128).c()
+    assert L.mx_gemm(ctypes.byref(fm), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
+    am = mx.MxQTensor(1024, 2048, None, 4096, None, None, 64, 256)
+    assert L.mx_gemm(ctypes.byref(fm), ctypes.byref(am), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
     # FP6 operands pass validation (checked here with a misaligned C, so no launch)
     for e in (mx.ELEM_FP6_E2M3, mx.ELEM_FP6_E3M2):
         g = mx.Format(elem=e).c()

@@ -199,6 +199,86 @@ def test_fp6_quantized_operands(ea, eb):
     assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref) + slack
 
 
+# ---- macro-block scaled MXFP4 ("Unveiling ... MXFP4", Sec. 4, MBS, Fig. 5) -----
+MBS_ORACLE = oracle.Format(macro_cols=128)
+MBS_DEV = mx.Format(macro_cols=128)
+
+
+def mbs_case(rng, rows, K, macro_codes):
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(118, 137, (rows, K // 32), dtype=np.uint8)
+    mac = rng.choice(np.asarray(macro_codes, np.uint8), (rows, K // 128))
+    deq = oracle.dequantize(MBS_ORACLE, {"codes": codes, "scales": scales, "macro_scales": mac}, rows, K)
+    q = make_q(codes, scales, rows, K)
+    q.macro_scales = torch.from_numpy(mac.reshape(-1).copy()).cuda()
+    return q, deq
+
+
+@pytest.mark.parametrize("side", ["both", "a", "b"])
+@pytest.mark.parametrize("M,N,K", [(130, 200, 1024), (64, 97, 384), (257, 33, 128)])
+def test_mbs_random(side, M, N, K):
+    rng = np.random.default_rng(M * 3 + K)
+    # UE4M3 codes of the macro scales the quantizer writes: 1, 1.125, ..., 2
+    macro = list(range(0x38, 0x41))
+    if side in ("both", "a"):
+        qa, da = mbs_case(rng, M, K, macro)
+        fa = MBS_DEV
+    else:
+        ca, sa = rng.integers(0, 256, (M, K // 2), dtype=np.uint8), rng.integers(118, 137, (M, K // 32), dtype=np.uint8)
+        qa, da, fa = make_q(ca, sa, M, K), ref_deq(ca, sa, M, K), mx.MXFP4
+    if side in ("both", "b"):
+        qb, db = mbs_case(rng, N, K, macro)
+        fb = MBS_DEV
+    else:
+        cb, sb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8), rng.integers(118, 137, (N, K // 32), dtype=np.uint8)
+        qb, db, fb = make_q(cb, sb, N, K), ref_deq(cb, sb, N, K), mx.MXFP4
+    ref = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert rel_frob(c32, ref) <= 1e-5
+    assert rel_frob(oracle.bf16_bits_to_f32(c16), oracle.bf16_bits_to_f32(bf16_of(ref))) <= 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 200, 1024), (33, 65, 256)])
+def test_mbs_exact_case(M, N, K):
+    """Unit E8M0 scales and macro scales of 1 and 2: every partial sum is a
+    multiple of 1/4 below 2^24 in magnitude, so the fp32 result is exact."""
+    rng = np.random.default_rng(K + 11)
+    qa, da = mbs_case(rng, M, K, [0x38, 0x40])
+    qb, db = mbs_case(rng, N, K, [0x38, 0x40])
+    for q, rows in ((qa, M), (qb, N)):
+        q.scales.fill_(127)
+    da = oracle.dequantize(MBS_ORACLE, {"codes": qa.codes.cpu().numpy().reshape(M, K // 2),
+                                        "scales": qa.scales.cpu().numpy().reshape(M, K // 32),
+                                        "macro_scales": qa.macro_scales.cpu().numpy().reshape(M, K // 128)}, M, K)
+    db = oracle.dequantize(MBS_ORACLE, {"codes": qb.codes.cpu().numpy().reshape(N, K // 2),
+                                        "scales": qb.scales.cpu().numpy().reshape(N, K // 32),
+                                        "macro_scales": qb.macro_scales.cpu().numpy().reshape(N, K // 128)}, N, K)
+    exact = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(MBS_DEV, qa, MBS_DEV, qb, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(c32, exact.astype(np.float32))
+
+
+def test_mbs_quantized_operands():
+    """Operands quantized on the GPU with 1 x 128 macro scales over 1 x 32 E8M0
+    sub-blocks; the product against the oracle's dequantized product, and the
+    product's fidelity (eq. (2)) not below plain MXFP4's."""
+    a, b = synth.w5(m=256, n=384, k=1024)
+    qa, _, _ = mx.mx_quantize(MBS_DEV, to_dev(a))
+    qb, _, _ = mx.mx_quantize(MBS_DEV, to_dev(b))
+    ra, rb = oracle.quantize(a, MBS_ORACLE), oracle.quantize(b, MBS_ORACLE)
+    ref = oracle.gemm_f64(ra["dequant"], rb["dequant"])
+    c32 = mx.mx_gemm(MBS_DEV, qa, MBS_DEV, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_frob(c32.cpu().numpy(), ref) <= 1e-5
+    R = oracle.gemm_f64(synth.bf16_bits_to_f32(a), synth.bf16_bits_to_f32(b)).astype(np.float32)
+    _, db_mbs = oracle.qsnr(R, c32.cpu().numpy())
+    q4a, _, _ = mx.mx_quantize(mx.MXFP4, to_dev(a))
+    q4b, _, _ = mx.mx_quantize(mx.MXFP4, to_dev(b))
+    _, db_4 = oracle.qsnr(R, mx.mx_gemm(mx.MXFP4, q4a, mx.MXFP4, q4b, out_dtype=torch.float32).cpu().numpy())
+    assert db_mbs > db_4
+
+
 def test_quantized_operands_and_qsnr_eq2():
     """W4A4 product of operands quantized on the GPU, and QSNR(AB) of eq. (2)
     ('Unveiling ... MXFP4', Sec. 3) against the bf16 product."""
