@@ -269,10 +269,18 @@ int mx_qsnr(int dtype, const void* ref, const void* approx, int64_t n, mx_stats*
 int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const mx_qtensor* b, void* c,
             int64_t ldc, int c_dtype, void* stream) {
     if (!fa || !fb || !a || !b) return MX_ERR_ARG;
-    for (const mx_format* f : {fa, fb}) {
-        if (!mxk::gemm_elem_ok(f->elem) || f->scale != MX_SCALE_E8M0 || f->block_rows != 1 ||
-            f->block_cols != 32 || f->asymmetric || f->hadamard)
-            return MX_ERR_UNSUPPORTED;
+    for (const mx_format* f : {fa, fb})
+        if (f->block_rows != 1 || f->asymmetric || f->hadamard) return MX_ERR_UNSUPPORTED;
+    // E8M0 scales on 1 x 32 blocks (MX): the scaled matrix instruction, any
+    // element pair of E2M1 / E2M3 / E3M2, macro scales allowed on MXFP4
+    const bool native = fa->scale == MX_SCALE_E8M0 && fb->scale == MX_SCALE_E8M0 && fa->block_cols == 32 &&
+                        fb->block_cols == 32 && mxk::gemm_elem_ok(fa->elem) && mxk::gemm_elem_ok(fb->elem);
+    if (!native) {
+        // E2M1 under E8M0, UE4M3, NVFP4 or UE5M3 scales on any row block:
+        // decoded to bf16 for the bf16 matrix instruction
+        for (const mx_format* f : {fa, fb})
+            if (f->elem != MX_ELEM_E2M1 || !mxk::gemm_upcvt_scale_ok(f->scale) || f->macro_cols)
+                return MX_ERR_UNSUPPORTED;
     }
     // macro-block scales: MXFP4 operands only (the sub-blocks are the 1 x 32
     // blocks the instruction scales)
@@ -291,13 +299,20 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     if (K == 0) return MX_ERR_UNSUPPORTED;
     if (!c || !a->codes || !a->scales || !b->codes || !b->scales) return MX_ERR_ARG;
     if ((fa->macro_cols && !a->macro_scales) || (fb->macro_cols && !b->macro_scales)) return MX_ERR_ARG;
+    if ((fa->scale == MX_SCALE_NVFP4 && !a->tensor_scale) || (fb->scale == MX_SCALE_NVFP4 && !b->tensor_scale))
+        return MX_ERR_ARG;
     if (!aligned16(c) || !aligned16(a->codes) || !aligned16(b->codes) || !aligned16(a->scales) ||
         !aligned16(b->scales))
         return MX_ERR_ALIGN;
-    return hip_status(mxk::launch_gemm(fa->elem, static_cast<const uint8_t*>(a->codes),
-                                       static_cast<const uint8_t*>(a->scales), fb->elem,
-                                       static_cast<const uint8_t*>(b->codes), static_cast<const uint8_t*>(b->scales),
-                                       c, M, N, K, ldc, c_dtype == MX_DTYPE_BF16, static_cast<hipStream_t>(stream),
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int cb = c_dtype == MX_DTYPE_BF16;
+    const uint8_t *ac = static_cast<const uint8_t*>(a->codes), *as = static_cast<const uint8_t*>(a->scales);
+    const uint8_t *bc = static_cast<const uint8_t*>(b->codes), *bs = static_cast<const uint8_t*>(b->scales);
+    if (!native)
+        return hip_status(mxk::launch_gemm_upcvt(
+            fa->scale, fa->block_cols, ac, as, fa->scale == MX_SCALE_NVFP4 ? a->tensor_scale : nullptr, fb->scale,
+            fb->block_cols, bc, bs, fb->scale == MX_SCALE_NVFP4 ? b->tensor_scale : nullptr, c, M, N, K, ldc, cb, s));
+    return hip_status(mxk::launch_gemm(fa->elem, ac, as, fb->elem, bc, bs, c, M, N, K, ldc, cb, s,
                                        fa->macro_cols ? static_cast<const uint8_t*>(a->macro_scales) : nullptr,
                                        fb->macro_cols ? static_cast<const uint8_t*>(b->macro_scales) : nullptr));
 }

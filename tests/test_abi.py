@@ -129,7 +129,7 @@ def test_quantize_rejects_before_launch():
 
 def test_gemm_rejects_before_launch():
     f = mx.Format().c()
-    bad = mx.Format(block_cols=16).c()
+    bad = mx.Format(elem=mx.ELEM_INT4).c()
     a = mx.MxQTensor(1024, 2048, None, None, None, None, 64, 256)
     b = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 256)
     b_k = mx.MxQTensor(4096, 8192, None, None, None, None, 32, 512)
@@ -151,7 +151,7 @@ def test_gemm_rejects_before_launch():
         g = mx.Format(elem=e).c()
         assert L.mx_gemm(ctypes.byref(g), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
                          mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
-    nv = mx.Format(scale=mx.SCALE_UE5M3).c()
+    nv = mx.Format(elem=mx.ELEM_E3M0, scale=mx.SCALE_UE5M3).c()
     assert L.mx_gemm(ctypes.byref(f), ctypes.byref(a), ctypes.byref(nv), ctypes.byref(b), 0x10000, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
     # macro-block scales: MXFP4 only, and the macro_scales buffer is required
@@ -163,6 +163,16 @@ def test_gemm_rejects_before_launch():
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
     am = mx.MxQTensor(1024, 2048, None, 4096, None, None, 64, 256)
     assert L.mx_gemm(ctypes.byref(fm), ctypes.byref(am), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
+    # FP6 elements need E8M0 scales on 1 x 32 blocks; NVFP4 needs its tensor scale
+    g6u = mx.Format(elem=mx.ELEM_FP6_E2M3, scale=mx.SCALE_UE4M3, block_cols=16).c()
+    assert L.mx_gemm(ctypes.byref(g6u), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    nvf = mx.Format(scale=mx.SCALE_NVFP4, block_cols=16).c()
+    assert L.mx_gemm(ctypes.byref(nvf), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
+    a_t = mx.MxQTensor(1024, 2048, None, None, 8192, None, 64, 256)
+    assert L.mx_gemm(ctypes.byref(nvf), ctypes.byref(a_t), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
     # FP6 operands pass validation (checked here with a misaligned C, so no launch)
     for e in (mx.ELEM_FP6_E2M3, mx.ELEM_FP6_E3M2):

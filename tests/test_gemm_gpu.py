@@ -279,6 +279,84 @@ def test_mbs_quantized_operands():
     assert db_mbs > db_4
 
 
+# ---- FP4 under UE4M3 / NVFP4 / UE5M3 / non-32 E8M0 blocks: bf16 decode path ----
+# (scale kind, block, unit scale code, codes drawn for random scales)
+UPC = {"nvfp4": (oracle.SC_NVFP4, 16, 0x38, (0x28, 0x48)), "ue4m3": (oracle.SC_UE4M3, 16, 0x38, (0x28, 0x48)),
+       "ue5m3": (oracle.SC_UE5M3, 16, 0x78, (0x68, 0x88)), "ue5m3_32": (oracle.SC_UE5M3, 32, 0x78, (0x68, 0x88)),
+       "e8m0_16": (oracle.SC_E8M0, 16, 127, (118, 137)), "e8m0_64": (oracle.SC_E8M0, 64, 127, (118, 137)),
+       "mxfp4": (oracle.SC_E8M0, 32, 127, (118, 137))}
+
+
+def upc_operand(rng, kind, rows, K, unit=False, g=None):
+    sc, bc, one, (lo, hi) = UPC[kind]
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = (np.full((rows, K // bc), one, np.uint8) if unit
+              else rng.integers(lo, hi, (rows, K // bc), dtype=np.uint8))
+    q = {"codes": codes, "scales": scales}
+    dq = make_q(codes, scales, rows, K)
+    if sc == oracle.SC_NVFP4:
+        gv = np.array([1.0 if unit else g], np.float32)
+        q["tensor_scale"] = gv
+        dq.tensor_scale = torch.from_numpy(gv).cuda()
+    fo = oracle.Format(scale=sc, block_cols=bc)
+    return dq, mx.Format(scale=sc, block_cols=bc), oracle.dequantize(fo, q, rows, K)
+
+
+UPC_PAIRS = [("nvfp4", "nvfp4"), ("ue4m3", "ue4m3"), ("ue5m3", "ue5m3"), ("ue5m3_32", "e8m0_16"),
+             ("e8m0_64", "e8m0_16"), ("nvfp4", "mxfp4"), ("mxfp4", "ue5m3")]
+
+
+@pytest.mark.parametrize("ka,kb", UPC_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(130, 200, 1024), (33, 65, 96), (40, 72, 192)])
+def test_upcvt_exact_case(ka, kb, M, N, K):
+    """Unit block scales (and tensor scales): every product of two E2M1 values
+    is a multiple of 1/4 and every partial sum is exact in fp32."""
+    if K % UPC[ka][1] or K % UPC[kb][1]:
+        pytest.skip("K is not a whole number of blocks")
+    rng = np.random.default_rng(M + K)
+    qa, fa, da = upc_operand(rng, ka, M, K, unit=True)
+    qb, fb, db = upc_operand(rng, kb, N, K, unit=True)
+    exact = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(c32, exact.astype(np.float32))
+    assert np.array_equal(c16, bf16_of(exact))
+
+
+@pytest.mark.parametrize("ka,kb", UPC_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(257, 130, 1024), (64, 96, 352)])
+def test_upcvt_random_scales(ka, kb, M, N, K):
+    if K % UPC[ka][1] or K % UPC[kb][1]:
+        pytest.skip("K is not a whole number of blocks")
+    rng = np.random.default_rng(K + 7)
+    qa, fa, da = upc_operand(rng, ka, M, K, g=3.0e-3)
+    qb, fb, db = upc_operand(rng, kb, N, K, g=0.37)
+    ref = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert rel_frob(c32, ref) <= 1e-5
+    assert rel_frob(oracle.bf16_bits_to_f32(c16), oracle.bf16_bits_to_f32(bf16_of(ref))) <= 1e-3
+
+
+def test_nvfp4_quantized_operands():
+    """NVFP4 operands quantized on the GPU (E2M1, UE4M3 per 16, fp32 tensor
+    scale): the product against the oracle's dequantized product; its QSNR
+    (eq. (2)) above MXFP4's on the same data ('Unveiling ... MXFP4', Sec. 3)."""
+    a, b = synth.w5(m=256, n=384, k=1024)
+    fmt, fo = mx.Format(scale=mx.SCALE_NVFP4, block_cols=16), oracle.Format(scale=oracle.SC_NVFP4, block_cols=16)
+    qa, _, _ = mx.mx_quantize(fmt, to_dev(a))
+    qb, _, _ = mx.mx_quantize(fmt, to_dev(b))
+    ref = oracle.gemm_f64(oracle.quantize(a, fo)["dequant"], oracle.quantize(b, fo)["dequant"])
+    c32 = mx.mx_gemm(fmt, qa, fmt, qb, out_dtype=torch.float32).cpu().numpy()
+    assert rel_frob(c32, ref) <= 1e-5
+    R = oracle.gemm_f64(synth.bf16_bits_to_f32(a), synth.bf16_bits_to_f32(b)).astype(np.float32)
+    q4a, _, _ = mx.mx_quantize(mx.MXFP4, to_dev(a))
+    q4b, _, _ = mx.mx_quantize(mx.MXFP4, to_dev(b))
+    _, db_nv = oracle.qsnr(R, c32)
+    _, db_4 = oracle.qsnr(R, mx.mx_gemm(mx.MXFP4, q4a, mx.MXFP4, q4b, out_dtype=torch.float32).cpu().numpy())
+    assert db_nv > db_4
+
+
 def test_quantized_operands_and_qsnr_eq2():
     """W4A4 product of operands quantized on the GPU, and QSNR(AB) of eq. (2)
     ('Unveiling ... MXFP4', Sec. 3) against the bf16 product."""
