@@ -12,7 +12,11 @@ scale per element) as `value`, GEMM TFLOP/s (2 M N K per product), each with
 its fraction of the MI355X peak, QSNR of A, B (eq. (1)) and of the product
 (eq. (2)) against the bf16 product, and the CPU oracle timed on this host.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+After the timed steps, the same product in the other block formats (MXFP6,
+mixed 6-/4-bit, MXFP4 with macro-block scales, NVFP4, UE5M3) is timed for
+information under "gemm_formats", with its QSNR (eq. (2)).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-formats]
 """
 import argparse
 import hashlib
@@ -23,7 +27,8 @@ import time
 
 M, N, K = 8192, 14336, 4096
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
-FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
+FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 (and FP6) MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, TFLOP/s
 QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 32
 
 
@@ -56,7 +61,51 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the products in the other block formats (not part of the step)")
     return ap.parse_args()
+
+
+def gemm_formats(mx, torch, a, b, C, R, dev, reps=5):
+    """The same product with operands in the other block formats the library
+    multiplies, for information (not part of the step): A and B quantized on the
+    GPU in each format, the product timed with events (median of `reps`), its
+    QSNR (eq. (2)) against the bf16 product R, and the fraction of the matrix
+    peak of the instruction the path runs on (FP4/FP6 10.1 PFLOP/s; the FP4
+    formats with fp8 block scales decode to bf16: 2.5 PFLOP/s)."""
+    F = mx.Format
+    fp6, fp6b = F(elem=mx.ELEM_FP6_E2M3), F(elem=mx.ELEM_FP6_E3M2)
+    nv = F(scale=mx.SCALE_NVFP4, block_cols=16)
+    cases = [
+        ("MXFP4 x MXFP4", mx.MXFP4, mx.MXFP4, "fp4 MFMA, LDS-staged", FP4_PEAK_TFLOPS),
+        ("MXFP6 E2M3 x MXFP6 E2M3", fp6, fp6, "fp6 MFMA, register-only", FP4_PEAK_TFLOPS),
+        ("MXFP6 E3M2 x MXFP6 E3M2", fp6b, fp6b, "fp6 MFMA, register-only", FP4_PEAK_TFLOPS),
+        ("MXFP6 E2M3 x MXFP4", fp6, mx.MXFP4, "fp6 x fp4 MFMA, register-only", FP4_PEAK_TFLOPS),
+        ("MXFP4-MBS x MXFP4-MBS", F(macro_cols=128), F(macro_cols=128), "fp4 MFMA + macro scales, register-only",
+         FP4_PEAK_TFLOPS),
+        ("NVFP4 x NVFP4", nv, nv, "bf16 MFMA after exact decode, register-only", BF16_PEAK_TFLOPS),
+        ("UE5M3/16 x UE5M3/16", F(scale=mx.SCALE_UE5M3, block_cols=16), F(scale=mx.SCALE_UE5M3, block_cols=16),
+         "bf16 MFMA after exact decode, register-only", BF16_PEAK_TFLOPS),
+    ]
+    out = []
+    for name, fa, fb, path, peak in cases:
+        qa, _, _ = mx.mx_quantize(fa, a)
+        qb, _, _ = mx.mx_quantize(fb, b)
+        mx.mx_gemm(fa, qa, fb, qb, c=C)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            mx.mx_gemm(fa, qa, fb, qb, c=C)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))[reps // 2]
+        _, db = mx.mx_qsnr(R, C.float())
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out.append({"operands": name, "path": path, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "frac_peak": round(tf / peak, 4), "peak_tflops": peak, "qsnr_ab_db": round(db, 4)})
+        del qa, qb
+    return out
 
 
 def main():
@@ -159,6 +208,7 @@ def main():
     qsnr = lambda st: 10 * np.log10(st["sig2"] / st["err2"])
     R = torch.matmul(A[0], B[0].t().contiguous()).float()     # bf16 reference product (hipBLASLt)
     _, qsnr_ab = mx.mx_qsnr(R, C.float())
+    variants = [] if args.no_formats else gemm_formats(mx, torch, A[0], B[0], C, R, dev)
     del R
 
     gt, qt = counted_traffic("gemm"), counted_traffic("quantize")
@@ -197,6 +247,7 @@ def main():
                               "traffic": None if qt is None else round(
                                   sum(qt[t]["fetch_bytes"] + qt[t]["write_bytes"] for t in ("A", "B")))},
         "qsnr_db": {"A": round(qsnr(st_a), 4), "B": round(qsnr(st_b), 4), "AB": round(qsnr_ab, 4)},
+        "gemm_formats": variants,
         "cpu_baseline": None,
     }
 
