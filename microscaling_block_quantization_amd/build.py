@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmx.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "quant_rows.hip", "quant_tiles.hip", "misc.hip", "gemm_mxfp4.hip", "gemm_upcvt.hip"]
+SOURCES = ["api.hip", "quant_rows.hip", "quant_tiles.hip", "misc.hip", "gemm_mxfp4.hip", "gemm_lds.hip", "gemm_upcvt.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

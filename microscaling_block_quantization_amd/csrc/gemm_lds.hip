@@ -1,0 +1,291 @@
+// gemm_lds.hip -- LDS-staged block-scaled GEMM for MXFP6 and mixed 4-/6-bit
+// operands: C = deq(A) . deq(B)^T with E8M0 scales per 1 x 32 block and each
+// operand's elements E2M1, E2M3 or E3M2, on V_MFMA_SCALE_F32_32X32X64_F8F6F4
+// (the 6-bit and mixed products of the ARITH 2025 MX-training report, main
+// results).
+//
+// A workgroup of 4 waves (2 x 2) computes a 128 x 128 tile; each wave owns 2 x 2
+// MFMA tiles of 32 x 32.  K advances 128 per stage (two 64-wide substeps); a
+// stage holds the tile's A and B codes, 64 bytes per row for E2M1 and 96 for
+// FP6.  Three stages form a ring in LDS, filled by LDS-DMA (buffer_load ...
+// lds, 16 bytes per lane) two stages ahead.  The 16-byte chunks of a row are
+// permuted by a row-dependent rotation (FP6) or XOR (E2M1) so that the chunk
+// reads of 8 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
+// codes, 24 bytes) spans one whole chunk and half of the next: one 16-byte
+// and one 8-byte read, put in order per lane.  The scales of a stage (4
+// bytes per row) are one dword load per row tile, a stage ahead.
+#include "mx_kernels.hpp"
+
+namespace mxk {
+using namespace mxd;
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int MF_E2M1 = 4;
+constexpr int lmf(int elem) { return elem == E2M1 ? 4 : elem == E2M3 ? 2 : 3; }
+
+template <int F>
+struct Op {
+    static constexpr int R = F == MF_E2M1 ? 64 : 96;   // bytes per row per stage
+    static constexpr int C = R / 16;                   // chunks per row
+    // physical chunk slot of logical chunk p in tile row r, and back
+    static __device__ __forceinline__ int phys(int r, int p) {
+        if constexpr (C == 4) return p ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+        else return (p + ((r >> 2) & 1)) % 6;
+    }
+    static __device__ __forceinline__ int logical(int r, int q) {
+        if constexpr (C == 4) return q ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+        else return (q + 6 - ((r >> 2) & 1)) % 6;
+    }
+};
+
+template <int FA_, int FB_>
+struct LGeo {
+    static constexpr int FA = FA_, FB = FB_;
+    static constexpr int BM = 128, BN = 128, BK = 128, NW = 4, D = 3;
+    static constexpr int SA = BM * Op<FA_>::R, SB = BN * Op<FB_>::R;
+    static constexpr int STAGE = SA + SB;
+    static constexpr int PA = SA / 1024, PB = SB / 1024;
+    static constexpr int PW = (PA + PB) / NW;          // DMA pieces per wave per stage
+    static_assert((PA + PB) % NW == 0, "DMA pieces split evenly over the waves");
+};
+
+__device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// one lane's operand for K block c (0..3) of the stage, tile row rr, from the
+// stage region `st` of its operand
+template <int F>
+__device__ __forceinline__ v8i frag(const uint8_t* __restrict__ st, int rr, int t, int half) {
+    using O = Op<F>;
+    v8i v;
+    if constexpr (F == MF_E2M1) {
+        const u32x4v x = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, 2 * t + half) * 16);
+        v[0] = (int)x[0]; v[1] = (int)x[1]; v[2] = (int)x[2]; v[3] = (int)x[3];
+        v[4] = 0; v[5] = 0;
+    } else {
+        // block 2t + h covers bytes [48t + 24h, +24): the whole chunk 3t + 2h
+        // and half h of chunk 3t + 1; lanes of half 0 take the whole chunk
+        // first, lanes of half 1 last
+        const u32x4v x = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, 3 * t + 2 * half) * 16);
+        const u32x2v y = *reinterpret_cast<const u32x2v*>(st + rr * O::R + O::phys(rr, 3 * t + 1) * 16 + 8 * half);
+        v[0] = (int)(half ? y[0] : x[0]);
+        v[1] = (int)(half ? y[1] : x[1]);
+        v[2] = (int)(half ? x[0] : x[2]);
+        v[3] = (int)(half ? x[1] : x[3]);
+        v[4] = (int)(half ? x[2] : y[0]);
+        v[5] = (int)(half ? x[3] : y[1]);
+    }
+    v[6] = 0;
+    v[7] = 0;
+    return v;
+}
+
+// substep T of a stage: K blocks 2T (lanes of half 0) and 2T + 1 (half 1);
+// this lane's scale byte is byte 2T of sc after the shift by 8 * half
+template <int T, int FA, int FB, int OFFB>
+__device__ __forceinline__ void substep(v16f (&acc)[2][2], const uint8_t* __restrict__ st, int ra, int rb, int half,
+                                        const int (&sc)[4]) {
+    v8i a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        a[i] = frag<FA>(st, ra + 32 * i, T, half);
+        b[i] = frag<FB>(st + OFFB, rb + 32 * i, T, half);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 2 * T, sc[i],
+                                                                       2 * T, sc[2 + j]);
+}
+
+// the operand panels of one tile: rows past M (N) read as zero through the
+// resource bounds; z is a zero-size resource for stages past K
+struct LPanels {
+    rsrc_t a, b, sa, sb, z;
+    int64_t rowa, rowb;
+    int kblocks, nst;
+};
+
+// DMA of stage s into its ring slot; stages past K go through the zero-size
+// resource (no memory access), so every stage issues the same count.  Piece g
+// of an operand covers 64 consecutive 16-byte LDS slots; the lane writing slot
+// (row r, physical chunk q) fetches the logical chunk stored there.
+template <class G>
+__device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s, int wave, int lane) {
+    // (device pass only: the host pass of this template rejects the LDS-DMA
+    // builtin, which would silently drop the kernels' launch stubs)
+#if defined(__HIP_DEVICE_COMPILE__)
+    using OA = Op<G::FA>;
+    using OB = Op<G::FB>;
+    uint8_t* slot = smem + (s % G::D) * G::STAGE;
+    const bool in = s < P.nst;
+#pragma unroll
+    for (int k = 0; k < G::PW; k++) {
+        const int g = wave * G::PW + k;                   // uniform
+        if (g < G::PA) {
+            const int f = g * 64 + lane, r = f / OA::C, q = f % OA::C;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.a : P.z, (lds_void*)(slot + g * 1024), 16,
+                                                     (int)(r * P.rowa) + OA::logical(r, q) * 16, s * OA::R, 0, 0);
+        } else {
+            const int h = g - G::PA;
+            const int f = h * 64 + lane, r = f / OB::C, q = f % OB::C;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.b : P.z, (lds_void*)(slot + G::SA + h * 1024), 16,
+                                                     (int)(r * P.rowb) + OB::logical(r, q) * 16, s * OB::R, 0, 0);
+        }
+    }
+#endif
+}
+
+// the 4 scale bytes of stage s for this lane's row tiles (A: 2, B: 2)
+__device__ __forceinline__ void stage_scales(uint32_t (&o)[4], const LPanels& P, int s, int ra, int rb) {
+    const bool in = s < P.nst;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        o[i] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sa : P.z, (ra + 32 * i) * P.kblocks + 4 * s, 0, 0);
+        o[2 + i] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sb : P.z, (rb + 32 * i) * P.kblocks + 4 * s, 0, 0);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// a bare workgroup barrier after this wave's LDS reads are done (the DMA the
+// barrier publishes was waited for with wait_vm)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// one stage: wait for its DMA and scales, free the slot two ahead, issue the
+// next stage's scales and the DMA two stages ahead, multiply
+template <class G>
+__device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s, int wave, int lane, int half, int ra,
+                                         int rb, v16f (&acc)[2][2], const uint32_t (&cur)[4], uint32_t (&nxt)[4]) {
+    wait_vm<G::PW>();
+    // every wave's share of stage s has landed and every wave is done
+    // reading slot (s + 2) % 3 (stage s - 1)
+    lds_barrier();
+    stage_scales(nxt, P, s + 1, ra, rb);
+    stage_dma<G>(smem, P, s + 2, wave, lane);
+    const uint8_t* st = smem + (s % G::D) * G::STAGE;
+    int sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) sc[i] = (int)(cur[i] >> (8 * half));
+    substep<0, G::FA, G::FB, G::SA>(acc, st, ra, rb, half, sc);
+    substep<1, G::FA, G::FB, G::SA>(acc, st, ra, rb, half, sc);
+}
+
+template <bool CBF16, int FA, int FB>
+__global__ __launch_bounds__(256, 2) void k_gemm_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
+                                                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
+                                                     void* __restrict__ C, int64_t M, int64_t N, int64_t K,
+                                                     int64_t ldc) {
+    using G = LGeo<FA, FB>;
+    using OA = Op<FA>;
+    using OB = Op<FB>;
+    constexpr int PW = G::PW, D = G::D;
+    static_assert(PW + 4 <= 63, "vmcnt");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5, lrow = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // tile order: slots dealt to the 8 XCDs round robin, so consecutive tiles
+    // of a grouped order land on one XCD and share A and B panels in its L2
+    const int tm = (int)((M + G::BM - 1) / G::BM), tn = (int)((N + G::BN - 1) / G::BN);
+    const int T = tm * tn;
+    int bid = blockIdx.x;
+    if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+    constexpr int GM = 8;
+    const int group = bid / (GM * tn), first = group * GM;
+    const int gsz = (tm - first) < GM ? (tm - first) : GM;
+    const int in_g = bid - group * GM * tn;
+    const int64_t m0 = (int64_t)(first + in_g % gsz) * G::BM, n0 = (int64_t)(in_g / gsz) * G::BN;
+
+    const int nst = (int)(K / G::BK);
+    const int kblocks = (int)(K / 32);
+    const int64_t rowa = (int64_t)kblocks * (FA == MF_E2M1 ? 16 : 24), rowb = (int64_t)kblocks * (FB == MF_E2M1 ? 16 : 24);
+    const int64_t va = M - m0 < G::BM ? M - m0 : G::BM, vb = N - n0 < G::BN ? N - n0 : G::BN;
+    const rsrc_t pa = rsrc(A + m0 * rowa, va * rowa), pb = rsrc(B + n0 * rowb, vb * rowb);
+    const rsrc_t psa = rsrc(SA + m0 * kblocks, va * kblocks), psb = rsrc(SB + n0 * kblocks, vb * kblocks);
+    const rsrc_t z = rsrc(A, 0);
+
+    const int ra = wm * 64 + lrow, rb = wn * 64 + lrow;
+    const LPanels P = {pa, pb, psa, psb, z, rowa, rowb, kblocks, nst};
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    uint32_t s0[4], s1[4];
+    stage_dma<G>(smem, P, 0, wave, lane);
+    stage_scales(s0, P, 0, ra, rb);
+    stage_dma<G>(smem, P, 1, wave, lane);
+    for (int s = 0; s < nst; s += 2) {
+        lds_step<G>(smem, P, s, wave, lane, half, ra, rb, acc, s0, s1);
+        if (s + 1 < nst) lds_step<G>(smem, P, s + 1, wave, lane, half, ra, rb, acc, s1, s0);
+    }
+    wait_vm<0>();
+
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t n = n0 + wn * 64 + 32 * j + lrow;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
+                if (m >= M) continue;
+                if constexpr (CBF16) static_cast<uint16_t*>(C)[m * ldc + n] = bf16_rne(acc[i][j][r]);
+                else static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
+            }
+        }
+}
+
+template <int FA, int FB>
+hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c, int64_t M,
+                        int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (c_bf16) k_gemm_lds<true, FA, FB><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    else k_gemm_lds<false, FA, FB><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_lds_b(int eb, const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c,
+                        int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    switch (lmf(eb)) {
+    case 4: return launch_lds_t<FA, 4>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 2: return launch_lds_t<FA, 2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    default: return launch_lds_t<FA, 3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_lds(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
+                           void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (K % 128) return hipErrorInvalidValue;
+    switch (lmf(ea)) {
+    case 4: return launch_lds_b<4>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 2: return launch_lds_b<2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    default: return launch_lds_b<3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    }
+}
+
+}  // namespace mxk

@@ -809,6 +809,8 @@ hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, cons
             k_gemm_tiled<false, false, G, GEMM_D><<<(unsigned)grid, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
         return hipGetLastError();
     }
+    // K a multiple of 128: the LDS-staged kernel for any element pair
+    if (K % 128 == 0) return launch_gemm_lds(ea, a, sa, eb, b, sb, c, M, N, K, ldc, c_bf16, s);
     switch (fmt_of(ea)) {
     case MF_E2M1: launch_simple_b<MF_E2M1>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
     case MF_E2M3: launch_simple_b<MF_E2M3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
