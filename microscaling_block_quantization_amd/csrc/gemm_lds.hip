@@ -4,15 +4,15 @@
 // (the 6-bit and mixed products of the ARITH 2025 MX-training report, main
 // results).
 //
-// A workgroup of 4 waves (2 x 2) computes a 128 x 128 tile; each wave owns 2 x 2
+// A workgroup of 8 waves (2 x 4) computes a 256 x 256 tile; each wave owns 4 x 2
 // MFMA tiles of 32 x 32.  K advances 128 per stage (two 64-wide substeps); a
 // stage holds the tile's A and B codes, 64 bytes per row for E2M1 and 96 for
 // FP6.  Three stages form a ring in LDS, filled by LDS-DMA (buffer_load ...
 // lds, 16 bytes per lane) two stages ahead.  The 16-byte chunks of a row are
 // permuted by a row-dependent rotation (FP6) or XOR (E2M1) so that the chunk
-// reads of 8 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
-// codes, 24 bytes) spans one whole chunk and half of the next: one 16-byte
-// and one 8-byte read, put in order per lane.  The scales of a stage (4
+// reads of 16 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
+// codes, 24 bytes) spans one whole chunk and half of the next: two 16-byte
+// reads, put in order per lane.  The scales of a stage (4
 // bytes per row) are one dword load per row tile, a stage ahead.
 #include "mx_kernels.hpp"
 
@@ -24,7 +24,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -36,20 +35,25 @@ struct Op {
     static constexpr int R = F == MF_E2M1 ? 64 : 96;   // bytes per row per stage
     static constexpr int C = R / 16;                   // chunks per row
     // physical chunk slot of logical chunk p in tile row r, and back
+    // FP6: a rotation by one slot in row quads 1 and 2 of every 16 rows; the
+    // 16-byte reads of one logical chunk by 16 consecutive rows then cover 64
+    // distinct banks (and those of 8 rows 32 banks)
+    static __device__ __forceinline__ int rot(int r) { return ((r >> 2) & 1) ^ ((r >> 3) & 1); }
     static __device__ __forceinline__ int phys(int r, int p) {
         if constexpr (C == 4) return p ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
-        else return (p + ((r >> 2) & 1)) % 6;
+        else return (p + rot(r)) % 6;
     }
     static __device__ __forceinline__ int logical(int r, int q) {
         if constexpr (C == 4) return q ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
-        else return (q + 6 - ((r >> 2) & 1)) % 6;
+        else return (q + 6 - rot(r)) % 6;
     }
 };
 
-template <int FA_, int FB_>
+template <int FA_, int FB_, int WGM_, int WGN_, int TI_, int TJ_>
 struct LGeo {
     static constexpr int FA = FA_, FB = FB_;
-    static constexpr int BM = 128, BN = 128, BK = 128, NW = 4, D = 3;
+    static constexpr int WGM = WGM_, WGN = WGN_, TI = TI_, TJ = TJ_;   // waves, MFMA tiles per wave
+    static constexpr int NW = WGM * WGN, BM = WGM * 32 * TI, BN = WGN * 32 * TJ, BK = 128, D = 3;
     static constexpr int SA = BM * Op<FA_>::R, SB = BN * Op<FB_>::R;
     static constexpr int STAGE = SA + SB;
     static constexpr int PA = SA / 1024, PB = SB / 1024;
@@ -73,12 +77,14 @@ __device__ __forceinline__ v8i frag(const uint8_t* __restrict__ st, int rr, int 
         v[4] = 0; v[5] = 0;
     } else {
         // block 2t + h covers bytes [48t + 24h, +24): the whole chunk 3t + 2h
-        // and half h of chunk 3t + 1; lanes of half 0 take the whole chunk
-        // first, lanes of half 1 last
+        // and half h of chunk 3t + 1.  Both halves read all of chunk 3t + 1
+        // (one logical chunk per read, so the rotation keeps it free of bank
+        // conflicts); half 0 puts its first 8 bytes after the whole chunk,
+        // half 1 its last 8 bytes before it
         const u32x4v x = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, 3 * t + 2 * half) * 16);
-        const u32x2v y = *reinterpret_cast<const u32x2v*>(st + rr * O::R + O::phys(rr, 3 * t + 1) * 16 + 8 * half);
-        v[0] = (int)(half ? y[0] : x[0]);
-        v[1] = (int)(half ? y[1] : x[1]);
+        const u32x4v y = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, 3 * t + 1) * 16);
+        v[0] = (int)(half ? y[2] : x[0]);
+        v[1] = (int)(half ? y[3] : x[1]);
         v[2] = (int)(half ? x[0] : x[2]);
         v[3] = (int)(half ? x[1] : x[3]);
         v[4] = (int)(half ? x[2] : y[0]);
@@ -91,21 +97,20 @@ __device__ __forceinline__ v8i frag(const uint8_t* __restrict__ st, int rr, int 
 
 // substep T of a stage: K blocks 2T (lanes of half 0) and 2T + 1 (half 1);
 // this lane's scale byte is byte 2T of sc after the shift by 8 * half
-template <int T, int FA, int FB, int OFFB>
-__device__ __forceinline__ void substep(v16f (&acc)[2][2], const uint8_t* __restrict__ st, int ra, int rb, int half,
-                                        const int (&sc)[4]) {
-    v8i a[2], b[2];
+template <int T, class G>
+__device__ __forceinline__ void substep(v16f (&acc)[G::TI][G::TJ], const uint8_t* __restrict__ st, int ra, int rb,
+                                        int half, const int (&sc)[G::TI + G::TJ]) {
+    v8i a[G::TI], b[G::TJ];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        a[i] = frag<FA>(st, ra + 32 * i, T, half);
-        b[i] = frag<FB>(st + OFFB, rb + 32 * i, T, half);
-    }
+    for (int i = 0; i < G::TI; i++) a[i] = frag<G::FA>(st, ra + 32 * i, T, half);
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int j = 0; j < G::TJ; j++) b[j] = frag<G::FB>(st + G::SA, rb + 32 * j, T, half);
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 2 * T, sc[i],
-                                                                       2 * T, sc[2 + j]);
+    for (int i = 0; i < G::TI; i++)
+#pragma unroll
+        for (int j = 0; j < G::TJ; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], G::FA, G::FB, 2 * T,
+                                                                       sc[i], 2 * T, sc[G::TI + j]);
 }
 
 // the operand panels of one tile: rows past M (N) read as zero through the
@@ -146,14 +151,16 @@ __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s
 #endif
 }
 
-// the 4 scale bytes of stage s for this lane's row tiles (A: 2, B: 2)
-__device__ __forceinline__ void stage_scales(uint32_t (&o)[4], const LPanels& P, int s, int ra, int rb) {
+// the 4 scale bytes of stage s for this lane's row tiles (A: TI, then B: TJ)
+template <class G>
+__device__ __forceinline__ void stage_scales(uint32_t (&o)[G::TI + G::TJ], const LPanels& P, int s, int ra, int rb) {
     const bool in = s < P.nst;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < G::TI; i++)
         o[i] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sa : P.z, (ra + 32 * i) * P.kblocks + 4 * s, 0, 0);
-        o[2 + i] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sb : P.z, (rb + 32 * i) * P.kblocks + 4 * s, 0, 0);
-    }
+#pragma unroll
+    for (int j = 0; j < G::TJ; j++)
+        o[G::TI + j] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sb : P.z, (rb + 32 * j) * P.kblocks + 4 * s, 0, 0);
 }
 
 template <int N>
@@ -169,36 +176,34 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // next stage's scales and the DMA two stages ahead, multiply
 template <class G>
 __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s, int wave, int lane, int half, int ra,
-                                         int rb, v16f (&acc)[2][2], const uint32_t (&cur)[4], uint32_t (&nxt)[4]) {
+                                         int rb, v16f (&acc)[G::TI][G::TJ], const uint32_t (&cur)[G::TI + G::TJ],
+                                         uint32_t (&nxt)[G::TI + G::TJ]) {
     wait_vm<G::PW>();
     // every wave's share of stage s has landed and every wave is done
     // reading slot (s + 2) % 3 (stage s - 1)
     lds_barrier();
-    stage_scales(nxt, P, s + 1, ra, rb);
+    stage_scales<G>(nxt, P, s + 1, ra, rb);
     stage_dma<G>(smem, P, s + 2, wave, lane);
     const uint8_t* st = smem + (s % G::D) * G::STAGE;
-    int sc[4];
+    int sc[G::TI + G::TJ];
 #pragma unroll
-    for (int i = 0; i < 4; i++) sc[i] = (int)(cur[i] >> (8 * half));
-    substep<0, G::FA, G::FB, G::SA>(acc, st, ra, rb, half, sc);
-    substep<1, G::FA, G::FB, G::SA>(acc, st, ra, rb, half, sc);
+    for (int i = 0; i < G::TI + G::TJ; i++) sc[i] = (int)(cur[i] >> (8 * half));
+    substep<0, G>(acc, st, ra, rb, half, sc);
+    substep<1, G>(acc, st, ra, rb, half, sc);
 }
 
-template <bool CBF16, int FA, int FB>
-__global__ __launch_bounds__(256, 2) void k_gemm_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
-                                                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
-                                                     void* __restrict__ C, int64_t M, int64_t N, int64_t K,
-                                                     int64_t ldc) {
-    using G = LGeo<FA, FB>;
-    using OA = Op<FA>;
-    using OB = Op<FB>;
-    constexpr int PW = G::PW, D = G::D;
-    static_assert(PW + 4 <= 63, "vmcnt");
+template <bool CBF16, class G>
+__global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_lds(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc) {
+    constexpr int FA = G::FA, FB = G::FB, TI = G::TI, TJ = G::TJ, D = G::D;
+    static_assert(G::PW + TI + TJ <= 63, "vmcnt");
+    static_assert(D * G::STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, lrow = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / G::WGN, wn = wave % G::WGN;
 
     // tile order: slots dealt to the 8 XCDs round robin, so consecutive tiles
     // of a grouped order land on one XCD and share A and B panels in its L2
@@ -220,19 +225,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(const uint8_t* __restrict__
     const rsrc_t psa = rsrc(SA + m0 * kblocks, va * kblocks), psb = rsrc(SB + n0 * kblocks, vb * kblocks);
     const rsrc_t z = rsrc(A, 0);
 
-    const int ra = wm * 64 + lrow, rb = wn * 64 + lrow;
+    const int ra = wm * 32 * TI + lrow, rb = wn * 32 * TJ + lrow;   // this lane's operand rows in the tile
     const LPanels P = {pa, pb, psa, psb, z, rowa, rowb, kblocks, nst};
-    v16f acc[2][2];
+    v16f acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TJ; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    uint32_t s0[4], s1[4];
+    uint32_t s0[TI + TJ], s1[TI + TJ];
     stage_dma<G>(smem, P, 0, wave, lane);
-    stage_scales(s0, P, 0, ra, rb);
+    stage_scales<G>(s0, P, 0, ra, rb);
     stage_dma<G>(smem, P, 1, wave, lane);
     for (int s = 0; s < nst; s += 2) {
         lds_step<G>(smem, P, s, wave, lane, half, ra, rb, acc, s0, s1);
@@ -241,14 +246,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(const uint8_t* __restrict__
     wait_vm<0>();
 
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t n = n0 + wn * 64 + 32 * j + lrow;
+        for (int j = 0; j < TJ; j++) {
+            const int64_t n = n0 + wn * 32 * TJ + 32 * j + lrow;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
+                const int64_t m = m0 + wm * 32 * TI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
                 if (m >= M) continue;
                 if constexpr (CBF16) static_cast<uint16_t*>(C)[m * ldc + n] = bf16_rne(acc[i][j][r]);
                 else static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
@@ -256,12 +261,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(const uint8_t* __restrict__
         }
 }
 
+#ifndef LDS_WGM
+#define LDS_WGM 2
+#define LDS_WGN 4
+#define LDS_TI 4
+#define LDS_TJ 2
+#endif
+
 template <int FA, int FB>
 hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c, int64_t M,
                         int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (c_bf16) k_gemm_lds<true, FA, FB><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
-    else k_gemm_lds<false, FA, FB><<<(unsigned)tiles, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    using G = LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ>;
+    const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
+    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
     return hipGetLastError();
 }
 
