@@ -185,21 +185,26 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
             void *stream);
 
 /* Block-scaled GEMM ([U] Sec. 3 Fig. 4, Sec. 4 Fig. 5): C = deq(A) . deq(B)^T
- * with A an M x K and B an N x K quantized tensor, each with E8M0 scales on
- * 1 x 32 row blocks along K (any E8M0 rule) and E2M1 (MXFP4) or FP6 E2M3 /
- * E3M2 (MXFP6) elements, the two operands' element types chosen
- * independently (the mixed 4-/6-bit products of [A], main results); fp32
+ * with A an M x K and B an N x K quantized tensor in row blocks along K; fp32
  * accumulation, C (M x N, row stride ldc elements) in bf16 (rounded to nearest
- * even) or fp32.  Runs on the gfx950 block-scaled FP8/FP6/FP4 matrix
- * instructions.  MXFP4 operands may carry macro-block scales (macro_cols
- * 128, [U] Sec. 4 MBS and Fig. 5: the partial product of each 128-wide K
- * step is multiplied by the two rows' UE4M3 macro scales); those products run
- * on the register-only kernel.  Other formats: MX_ERR_UNSUPPORTED (macro
- * scales with FP6 elements included).  Shapes: K % 32 == 0, as
- * the 1 x 32 blocks require (MX_ERR_ARG otherwise); MXFP4 x MXFP4 without
- * macro scales and with K a multiple of 1024 takes the LDS-staged kernel,
- * every other case a register-only one; any M, N.  macro_scales must be set
- * when the format has macro_cols (MX_ERR_ARG).                                              */
+ * even) or fp32.  Formats, per operand:
+ *  - E8M0 scales on 1 x 32 blocks (any rule) with E2M1 (MXFP4) or FP6 E2M3 /
+ *    E3M2 (MXFP6) elements, chosen independently for A and B (the mixed
+ *    4-/6-bit products of [A], main results): the gfx950 block-scaled
+ *    FP8/FP6/FP4 matrix instruction.  MXFP4 operands may carry macro-block
+ *    scales (macro_cols 128, [U] Sec. 4 MBS and Fig. 5: each 128-wide K step's
+ *    partial product is multiplied by the two rows' UE4M3 macro scales).
+ *  - E2M1 elements under UE4M3, NVFP4 (UE4M3 + fp32 tensor scale), UE5M3 or
+ *    E8M0 scales on 1 x b blocks, b a multiple of 8 (when the other operand
+ *    is not of the kind above): each lane decodes its codes to bf16 exactly
+ *    and the bf16 matrix instruction multiplies.
+ * Anything else (INT4 / E3M0 elements, asymmetric, rotated, column or 2D
+ * blocks, macro scales on FP6): MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
+ * whole blocks (MX_ERR_ARG otherwise); any M, N.  E8M0 products with K a
+ * multiple of 128 run on LDS-staged kernels (MXFP4 x MXFP4 without macro
+ * scales and K a multiple of 1024 on the most tuned one), other K and the
+ * fp8-scaled formats on register-only kernels.  macro_scales must be set when
+ * the format has macro_cols, tensor_scale for NVFP4 (MX_ERR_ARG).          */
 int mx_gemm(const mx_format *fa, const mx_qtensor *a, const mx_format *fb,
             const mx_qtensor *b, void *c, int64_t ldc, int c_dtype, void *stream);
 

@@ -49,13 +49,19 @@ struct Op {
     }
 };
 
-template <int FA_, int FB_, int WGM_, int WGN_, int TI_, int TJ_>
+template <int FA_, int FB_, int WGM_, int WGN_, int TI_, int TJ_, int MBS_ = 0>
 struct LGeo {
-    static constexpr int FA = FA_, FB = FB_;
+    static constexpr int FA = FA_, FB = FB_, MBS = MBS_;
     static constexpr int WGM = WGM_, WGN = WGN_, TI = TI_, TJ = TJ_;   // waves, MFMA tiles per wave
     static constexpr int NW = WGM * WGN, BM = WGM * 32 * TI, BN = WGN * 32 * TJ, BK = 128, D = 3;
     static constexpr int SA = BM * Op<FA_>::R, SB = BN * Op<FB_>::R;
-    static constexpr int STAGE = SA + SB;
+    // macro-block scales (MBS bit 0: A, bit 1: B; a stage is one 128-wide
+    // macro block): each lane loads the bytes of its operand rows with the
+    // stage's E8M0 scales; A's go through LDS (BM bytes after the codes) to
+    // the lanes that hold those rows' accumulators
+    static constexpr int NS = (TI + TJ) * (MBS ? 2 : 1);   // scale registers per stage
+    static constexpr int OFF_M = SA + SB;
+    static constexpr int STAGE = OFF_M + ((MBS & 1) ? BM : 0);
     static constexpr int PA = SA / 1024, PB = SB / 1024;
     static constexpr int PW = (PA + PB) / NW;          // DMA pieces per wave per stage
     static_assert((PA + PB) % NW == 0, "DMA pieces split evenly over the waves");
@@ -116,9 +122,9 @@ __device__ __forceinline__ void substep(v16f (&acc)[G::TI][G::TJ], const uint8_t
 // the operand panels of one tile: rows past M (N) read as zero through the
 // resource bounds; z is a zero-size resource for stages past K
 struct LPanels {
-    rsrc_t a, b, sa, sb, z;
+    rsrc_t a, b, sa, sb, z, ma, mb;
     int64_t rowa, rowb;
-    int kblocks, nst;
+    int kblocks, nst, mcols;
 };
 
 // DMA of stage s into its ring slot; stages past K go through the zero-size
@@ -127,6 +133,7 @@ struct LPanels {
 // (row r, physical chunk q) fetches the logical chunk stored there.
 template <class G>
 __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s, int wave, int lane) {
+
     // (device pass only: the host pass of this template rejects the LDS-DMA
     // builtin, which would silently drop the kernels' launch stubs)
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -151,9 +158,10 @@ __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s
 #endif
 }
 
-// the 4 scale bytes of stage s for this lane's row tiles (A: TI, then B: TJ)
+// the 4 scale bytes of stage s for this lane's row tiles (A: TI, then B:
+// TJ), then (MBS) the macro scale byte of each of those rows
 template <class G>
-__device__ __forceinline__ void stage_scales(uint32_t (&o)[G::TI + G::TJ], const LPanels& P, int s, int ra, int rb) {
+__device__ __forceinline__ void stage_scales(uint32_t (&o)[G::NS], const LPanels& P, int s, int ra, int rb) {
     const bool in = s < P.nst;
 #pragma unroll
     for (int i = 0; i < G::TI; i++)
@@ -161,6 +169,24 @@ __device__ __forceinline__ void stage_scales(uint32_t (&o)[G::TI + G::TJ], const
 #pragma unroll
     for (int j = 0; j < G::TJ; j++)
         o[G::TI + j] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sb : P.z, (rb + 32 * j) * P.kblocks + 4 * s, 0, 0);
+    if constexpr (G::MBS != 0) {
+        constexpr int B0 = G::TI + G::TJ;
+#pragma unroll
+        for (int i = 0; i < G::TI; i++)
+            o[B0 + i] = (G::MBS & 1) ? __builtin_amdgcn_raw_buffer_load_b8(in ? P.ma : P.z, (ra + 32 * i) * P.mcols + s, 0, 0)
+                                     : 0x38u;
+#pragma unroll
+        for (int j = 0; j < G::TJ; j++)
+            o[B0 + G::TI + j] =
+                (G::MBS & 2) ? __builtin_amdgcn_raw_buffer_load_b8(in ? P.mb : P.z, (rb + 32 * j) * P.mcols + s, 0, 0)
+                             : 0x38u;
+    }
+}
+
+// value of a UE4M3 macro-block scale code (E4M3 bits, bias 7, sign clear)
+__device__ __forceinline__ float ue4m3(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
 }
 
 template <int N>
@@ -176,9 +202,16 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // next stage's scales and the DMA two stages ahead, multiply
 template <class G>
 __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s, int wave, int lane, int half, int ra,
-                                         int rb, v16f (&acc)[G::TI][G::TJ], const uint32_t (&cur)[G::TI + G::TJ],
-                                         uint32_t (&nxt)[G::TI + G::TJ]) {
+                                         int rb, v16f (&acc)[G::TI][G::TJ], const uint32_t (&cur)[G::NS],
+                                         uint32_t (&nxt)[G::NS]) {
     wait_vm<G::PW>();
+    if constexpr ((G::MBS & 1) != 0) {
+        // A's macro bytes of stage s to LDS for the accumulator rows (waves
+        // that share A rows write the same values)
+        uint8_t* ms = smem + (s % G::D) * G::STAGE + G::OFF_M;
+#pragma unroll
+        for (int i = 0; i < G::TI; i++) ms[ra + 32 * i] = (uint8_t)cur[G::TI + G::TJ + i];
+    }
     // every wave's share of stage s has landed and every wave is done
     // reading slot (s + 2) % 3 (stage s - 1)
     lds_barrier();
@@ -188,16 +221,53 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
     int sc[G::TI + G::TJ];
 #pragma unroll
     for (int i = 0; i < G::TI + G::TJ; i++) sc[i] = (int)(cur[i] >> (8 * half));
-    substep<0, G>(acc, st, ra, rb, half, sc);
-    substep<1, G>(acc, st, ra, rb, half, sc);
+    if constexpr (G::MBS == 0) {
+        substep<0, G>(acc, st, ra, rb, half, sc);
+        substep<1, G>(acc, st, ra, rb, half, sc);
+    } else {
+        // the stage's product into fresh accumulators, then added to the total
+        // times the macro scales of the accumulator's rows (A) and column (B);
+        // their product is exact in fp32
+        v16f t[G::TI][G::TJ];
+#pragma unroll
+        for (int i = 0; i < G::TI; i++)
+#pragma unroll
+            for (int j = 0; j < G::TJ; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) t[i][j][r] = 0.f;
+        substep<0, G>(t, st, ra, rb, half, sc);
+        substep<1, G>(t, st, ra, rb, half, sc);
+        const uint8_t* ms = st + G::OFF_M;
+        float fb[G::TJ];
+#pragma unroll
+        for (int j = 0; j < G::TJ; j++) fb[j] = ue4m3(cur[2 * G::TI + G::TJ + j]);
+#pragma unroll
+        for (int i = 0; i < G::TI; i++) {
+            // accumulator register 4q + p holds row 8q + 4 half + p of the tile
+            const int r0 = ra - (ra & 31) + 4 * half;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t w = 0x38383838u;                 // four codes of 1.0
+                if constexpr ((G::MBS & 1) != 0) w = *reinterpret_cast<const uint32_t*>(ms + r0 + 32 * i + 8 * q);
+#pragma unroll
+                for (int p = 0; p < 4; p++) {
+                    const float fa = ue4m3((w >> (8 * p)) & 0xffu);
+#pragma unroll
+                    for (int j = 0; j < G::TJ; j++)
+                        acc[i][j][4 * q + p] = __builtin_fmaf(t[i][j][4 * q + p], fa * fb[j], acc[i][j][4 * q + p]);
+                }
+            }
+        }
+    }
 }
 
 template <bool CBF16, class G>
 __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_lds(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc) {
+    const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc,
+    const uint8_t* __restrict__ MA, const uint8_t* __restrict__ MB) {
     constexpr int FA = G::FA, FB = G::FB, TI = G::TI, TJ = G::TJ, D = G::D;
-    static_assert(G::PW + TI + TJ <= 63, "vmcnt");
+    static_assert(G::PW + G::NS <= 63, "vmcnt");
     static_assert(D * G::STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
     const int lane = threadIdx.x & 63;
@@ -224,9 +294,12 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
     const rsrc_t pa = rsrc(A + m0 * rowa, va * rowa), pb = rsrc(B + n0 * rowb, vb * rowb);
     const rsrc_t psa = rsrc(SA + m0 * kblocks, va * kblocks), psb = rsrc(SB + n0 * kblocks, vb * kblocks);
     const rsrc_t z = rsrc(A, 0);
+    const int mcols = (int)(K / 128);
+    const rsrc_t pma = (G::MBS & 1) ? rsrc(MA + m0 * mcols, va * mcols) : z;
+    const rsrc_t pmb = (G::MBS & 2) ? rsrc(MB + n0 * mcols, vb * mcols) : z;
 
     const int ra = wm * 32 * TI + lrow, rb = wn * 32 * TJ + lrow;   // this lane's operand rows in the tile
-    const LPanels P = {pa, pb, psa, psb, z, rowa, rowb, kblocks, nst};
+    const LPanels P = {pa, pb, psa, psb, z, pma, pmb, rowa, rowb, kblocks, nst, mcols};
     v16f acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; i++)
@@ -235,7 +308,7 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    uint32_t s0[TI + TJ], s1[TI + TJ];
+    uint32_t s0[G::NS], s1[G::NS];
     stage_dma<G>(smem, P, 0, wave, lane);
     stage_scales<G>(s0, P, 0, ra, rb);
     stage_dma<G>(smem, P, 1, wave, lane);
@@ -273,8 +346,22 @@ hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
                         int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
     using G = LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ>;
     const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
-    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
-    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc);
+    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, nullptr, nullptr);
+    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+// MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): 128 x 128
+// tiles (4 waves of 2 x 2 MFMA tiles), leaving registers for the per-stage
+// accumulators
+template <int MBS>
+hipError_t launch_lds_mbs_t(const uint8_t* a, const uint8_t* sa, const uint8_t* ma, const uint8_t* b,
+                            const uint8_t* sb, const uint8_t* mb, void* c, int64_t M, int64_t N, int64_t K,
+                            int64_t ldc, int c_bf16, hipStream_t s) {
+    using G = LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS>;
+    const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
+    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
+    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
     return hipGetLastError();
 }
 
@@ -291,9 +378,16 @@ hipError_t launch_lds_b(int eb, const uint8_t* a, const uint8_t* sa, const uint8
 }  // namespace
 
 hipError_t launch_gemm_lds(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
-                           void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+                           void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
+                           const uint8_t* ma, const uint8_t* mb) {
     if (M == 0 || N == 0) return hipSuccess;
     if (K % 128) return hipErrorInvalidValue;
+    if (ma || mb) {
+        if (ea != E2M1 || eb != E2M1) return hipErrorInvalidValue;
+        if (ma && mb) return launch_lds_mbs_t<3>(a, sa, ma, b, sb, mb, c, M, N, K, ldc, c_bf16, s);
+        if (ma) return launch_lds_mbs_t<1>(a, sa, ma, b, sb, mb, c, M, N, K, ldc, c_bf16, s);
+        return launch_lds_mbs_t<2>(a, sa, ma, b, sb, mb, c, M, N, K, ldc, c_bf16, s);
+    }
     switch (lmf(ea)) {
     case 4: return launch_lds_b<4>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
     case 2: return launch_lds_b<2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);

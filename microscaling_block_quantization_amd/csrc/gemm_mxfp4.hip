@@ -63,25 +63,12 @@ __device__ __forceinline__ v8i zero_block() {
     return v;
 }
 
-// value of a UE4M3 macro-block scale code (E4M3 bits, bias 7, sign clear)
-__device__ __forceinline__ float ue4m3_value(uint32_t c) {
-    const uint32_t e = c >> 3, m = c & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-}
-
 // Register-only kernel, any element pair: 4 waves of 64 x 64 outputs (2 x 2
-// MFMA tiles), operands straight from global memory.  MBS (bit 0: A, bit 1: B)
-// marks operands with macro-block scales, one UE4M3 value per row per 128 K
-// ("Unveiling the Potential of Quantization with MXFP4", Sec. 4, Macro Block
-// Scaling and its Fig. 5): each 128-wide K step is then multiplied into a
-// fresh accumulator and added to the total times the two rows' macro scales,
-// whose product is exact in fp32.
-template <bool CBF16, int FA, int FB, int MBS = 0>
+// MFMA tiles), operands straight from global memory.
+template <bool CBF16, int FA, int FB>
 __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
-                                                     void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc,
-                                                     const uint8_t* __restrict__ MA = nullptr,
-                                                     const uint8_t* __restrict__ MBp = nullptr) {
+                                                     void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, row = lane & 31;
     const int64_t m0 = (int64_t)blockIdx.y * TM + (wave >> 1) * 64;
@@ -125,44 +112,15 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
             sa[i] = (int)(ca[0] | (ca[1] << 16));
             sb[i] = (int)(cb[0] | (cb[1] << 16));
         }
-        if constexpr (MBS != 0) {
-            // macro scales of this lane's accumulator rows (A) and column (B)
-            // for macro block k0 / 128
-            const int64_t mcols = K / 128, mk = k0 / 128;
-            float fa[2][16], fb[2];
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    int64_t m = m0 + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
-                    m = m < M ? m : M - 1;
-                    fa[i][r] = (MBS & 1) ? ue4m3_value(MA[m * mcols + mk]) : 1.0f;
-                }
-                fb[i] = (MBS & 2) ? ue4m3_value(MBp[rb[i] * mcols + mk]) : 1.0f;
+            for (int j = 0; j < 2; j++) {
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av[i][0], bv[j][0], acc[i][j], FA, FB, 0, sa[i], 0, sb[j]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av[i][1], bv[j][1], acc[i][j], FA, FB, 2, sa[i], 2, sb[j]);
             }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    v16f t;
-#pragma unroll
-                    for (int r = 0; r < 16; r++) t[r] = 0.f;
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i][0], bv[j][0], t, FA, FB, 0, sa[i], 0, sb[j]);
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i][1], bv[j][1], t, FA, FB, 2, sa[i], 2, sb[j]);
-#pragma unroll
-                    for (int r = 0; r < 16; r++) acc[i][j][r] = __builtin_fmaf(t[r], fa[i][r] * fb[j], acc[i][j][r]);
-                }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av[i][0], bv[j][0], acc[i][j], FA, FB, 0, sa[i], 0, sb[j]);
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av[i][1], bv[j][1], acc[i][j], FA, FB, 2, sa[i], 2, sb[j]);
-                }
-        }
     }
 
 #pragma unroll
@@ -770,17 +728,9 @@ hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, cons
     if (M == 0 || N == 0) return hipSuccess;
     if (!gemm_elem_ok(ea) || !gemm_elem_ok(eb)) return hipErrorInvalidValue;
     if (ma || mb) {
-        // macro-block scaled MXFP4: register-only kernel
+        // macro-block scaled MXFP4 (K is a multiple of 128 with macro blocks)
         if (ea != E2M1 || eb != E2M1 || K % 128) return hipErrorInvalidValue;
-        dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
-        const int mbs = (ma ? 1 : 0) | (mb ? 2 : 0);
-#define MX_MBS_CASE(Cv, Mv) \
-        if (!!c_bf16 == (Cv) && mbs == (Mv)) \
-            k_gemm_simple<Cv, MF_E2M1, MF_E2M1, Mv><<<grid, 256, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
-        MX_MBS_CASE(true, 1) MX_MBS_CASE(true, 2) MX_MBS_CASE(true, 3)
-        MX_MBS_CASE(false, 1) MX_MBS_CASE(false, 2) MX_MBS_CASE(false, 3)
-#undef MX_MBS_CASE
-        return hipGetLastError();
+        return launch_gemm_lds(ea, a, sa, eb, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
     }
     // the tiled kernel (E2M1 operands) fetches scales in 32-byte row groups (8
     // stages of 128): with K a multiple of 1024 every scale row starts 32-byte

@@ -62,8 +62,10 @@ hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, cons
                        void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
                        const uint8_t* ma = nullptr, const uint8_t* mb = nullptr);
 // LDS-staged kernel for E8M0 1 x 32 operands of any element pair, K % 128 == 0
+// (ma / mb: UE4M3 macro-block scales per 1 x 128, E2M1 operands only; nullable)
 hipError_t launch_gemm_lds(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
-                           void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s);
+                           void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
+                           const uint8_t* ma = nullptr, const uint8_t* mb = nullptr);
 // E2M1 operands under E8M0 / UE4M3 / NVFP4 / UE5M3 scales on 1 x bc blocks
 // (bc a multiple of 8), decoded to bf16; ta / tb: per-tensor scales or null
 bool gemm_upcvt_scale_ok(int scale);
