@@ -21,6 +21,8 @@
 // instructions of a 64-wide K step: the 16 code bytes of k0 + 32 h .. + 31,
 // one load, and every group of 8 lies inside one block (blocks are multiples
 // of 8 wide).
+#include <type_traits>
+
 #include "mx_kernels.hpp"
 
 namespace mxk {
@@ -165,6 +167,308 @@ __global__ __launch_bounds__(256) void k_gemm_upcvt(UOperand A, UOperand B, cons
 
 int ukind(int scale) { return scale == SC_E8M0 ? UK_E8M0 : scale == SC_UE5M3 ? UK_UE5M3 : UK_UE4M3; }
 
+// ---------------------------------------------------------------------------
+// LDS-staged form for 1 x 16 and 1 x 32 blocks with K a multiple of 128: 256 x
+// 256 tiles of 8 waves (4 x 2 MFMA tiles each), 128-wide K stages of codes (64
+// bytes per row, four 16-byte chunks XOR-permuted per row so the chunk reads
+// of 16 consecutive rows hit distinct banks) in a three-deep LDS ring filled
+// by LDS-DMA two stages ahead; the stage's block scales (8 bytes per row at
+// most) are one load per row tile, a stage ahead.  Each lane decodes its
+// 32-code chunk group by group, without branches, and feeds the instruction
+// right away.
+//
+// Two routes.  When both operands carry UE4M3 scales (NVFP4, with or without
+// its tensor scale) every product q * s has at most five significant bits and
+// lies in [2^-10, 2688]: exact in fp16, so the codes are decoded to fp16 (the
+// convert scaled by 2^8, times the scale code shifted into an fp16 bit pattern,
+// which is s * 2^-8) and multiplied by the fp16 instruction at the bf16 rate,
+// 8 vector operations per 8 codes.  Otherwise (E8M0 or UE5M3 scales on either
+// side: products span more binades than fp16 holds) they go to bf16: E8M0 by
+// the power-of-two scaled convert, 4 operations per 8 codes; UE4M3 / UE5M3 by
+// an fp32 decode times s, narrowed exactly, 16 operations.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+constexpr int UWGM = 2, UWGN = 4, UTI = 4, UTJ = 2, UNW = UWGM * UWGN;
+constexpr int UBM = UWGM * 32 * UTI, UBN = UWGN * 32 * UTJ, UD = 3;
+constexpr int USA = UBM * 64, USTAGE = (UBM + UBN) * 64;
+constexpr int UPW = USTAGE / 1024 / UNW;               // DMA pieces per wave per stage
+
+// operand decode kinds of the LDS kernel
+enum { DK_E8M0 = 0, DK_FP8 = 1, DK_F16 = 2 };
+
+__device__ __forceinline__ int uphys(int r, int p) { return p ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)); }
+
+__device__ __forceinline__ rsrc_t ursrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// per-operand constants of the decode
+struct UDec {
+    float mul;          // DK_FP8: 2^(127 - bias)
+    uint32_t nan;       // DK_FP8 / DK_F16: the scale code that means NaN
+    int lg;             // log2 of the block width (4 or 5)
+};
+
+struct UPanels {
+    rsrc_t a, b, sa, sb, z;
+    int rowb, srowa, srowb, spa, spb, nst;              // code row bytes; scale row and stage bytes of A, B
+};
+
+template <int N>
+__device__ __forceinline__ void uwait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void ubarrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// DMA of stage s (device pass only: the host pass rejects the LDS-DMA builtin
+// in a template and would drop the launch stubs)
+__device__ __forceinline__ void ustage_dma(uint8_t* smem, const UPanels& P, int s, int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint8_t* slot = smem + (s % UD) * USTAGE;
+    const bool in = s < P.nst;
+#pragma unroll
+    for (int k = 0; k < UPW; k++) {
+        const int g = wave * UPW + k;                    // uniform
+        if (g < USA / 1024) {
+            const int f = g * 64 + lane, r = f >> 2, q = f & 3;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.a : P.z, (lds_void*)(slot + g * 1024), 16,
+                                                     r * P.rowb + uphys(r, q) * 16, s * 64, 0, 0);
+        } else {
+            const int h = g - USA / 1024;
+            const int f = h * 64 + lane, r = f >> 2, q = f & 3;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.b : P.z, (lds_void*)(slot + USA + h * 1024), 16,
+                                                     r * P.rowb + uphys(r, q) * 16, s * 64, 0, 0);
+        }
+    }
+#endif
+}
+
+// the block scales of stage s for this lane's rows (8 bytes for 1 x 16
+// blocks, 4 for 1 x 32), A's row tiles then B's
+__device__ __forceinline__ uint64_t urow_scales(rsrc_t r, int off, int sp) {
+    if (sp == 8) return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ void ustage_scales(uint64_t (&o)[UTI + UTJ], const UPanels& P, int s, int ra, int rb) {
+    const bool in = s < P.nst;
+#pragma unroll
+    for (int i = 0; i < UTI; i++) o[i] = urow_scales(in ? P.sa : P.z, (ra + 32 * i) * P.srowa + P.spa * s, P.spa);
+#pragma unroll
+    for (int j = 0; j < UTJ; j++)
+        o[UTI + j] = urow_scales(in ? P.sb : P.z, (rb + 32 * j) * P.srowb + P.spb * s, P.spb);
+}
+
+// eight fp16 products q * s of the codes in dword w; h holds s * 2^-8 twice
+template <int BYTE>
+__device__ __forceinline__ h2v dec2_f16(uint32_t w, h2v h) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, BYTE) * h;
+}
+__device__ __forceinline__ h8v dec8_f16(uint32_t w, h2v h) {
+    const h2v p0 = dec2_f16<0>(w, h), p1 = dec2_f16<1>(w, h), p2 = dec2_f16<2>(w, h), p3 = dec2_f16<3>(w, h);
+    h8v v;
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+    return v;
+}
+
+// scale operand of one group for each kind: E8M0 an fp32 power of two (code
+// 0: 2^-127; 255: NaN); FP8 the fp32 value (subnormal codes through an fp32
+// subnormal times 2^(127 - bias), exact); F16 the UE4M3 code's fp16 pattern
+// (s * 2^-8, the exponent bias difference) in both halves
+template <int DK>
+__device__ __forceinline__ uint32_t uscale_bits(uint32_t c, const UDec& d) {
+    if constexpr (DK == DK_E8M0) {
+        const uint32_t v = c ? c << 23 : 0x00400000u;
+        return c == 255u ? 0x7fc00000u : v;
+    } else if constexpr (DK == DK_FP8) {
+        const float v = __uint_as_float(c << 20) * d.mul;
+        return c == d.nan ? 0x7fc00000u : __float_as_uint(v);
+    } else {
+        const uint32_t v = c == d.nan ? 0x7e00u : c << 7;
+        return v | (v << 16);
+    }
+}
+
+template <int DK>
+struct UVec {
+    typedef typename std::conditional<DK == DK_F16, h8v, bf8v>::type type;
+};
+
+template <int DK>
+__device__ __forceinline__ typename UVec<DK>::type udecode(uint32_t w, uint32_t sb) {
+    if constexpr (DK == DK_E8M0) return decode8_pow2(w, __uint_as_float(sb));
+    else if constexpr (DK == DK_FP8) return decode8(w, __uint_as_float(sb));
+    else return dec8_f16(w, __builtin_bit_cast(h2v, sb));
+}
+
+// the scale byte of group q (8 codes) of this lane's chunk, from the chunk's
+// scale bytes x (1 x 16 blocks: 2 bytes; 1 x 32: 1)
+__device__ __forceinline__ uint32_t ugroup_code(uint32_t x, int q, int lg) {
+    return (x >> (8 * ((q >> 1) & (lg == 4 ? 1 : 0)))) & 0xffu;
+}
+
+template <int KA, int KB>
+__device__ __forceinline__ void ustep(uint8_t* smem, const UPanels& P, int s, int wave, int lane, int half, int ra,
+                                      int rb, const UDec& da, const UDec& db, v16f (&acc)[UTI][UTJ],
+                                      const uint64_t (&cur)[UTI + UTJ], uint64_t (&nxt)[UTI + UTJ]) {
+    uwait_vm<UPW>();
+    ubarrier();
+    ustage_scales(nxt, P, s + 1, ra, rb);
+    ustage_dma(smem, P, s + 2, wave, lane);
+    const uint8_t* st = smem + (s % UD) * USTAGE;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int c = 2 * t + half;
+        // first scale byte of chunk c: block (32 c) >> lg of the stage
+        const int sha = 8 * ((32 * c) >> da.lg), shb = 8 * ((32 * c) >> db.lg);
+        u32x4v xa[UTI], xb[UTJ];
+        uint32_t ca[UTI], cb[UTJ];
+#pragma unroll
+        for (int i = 0; i < UTI; i++) {
+            const int r = ra + 32 * i;
+            xa[i] = *reinterpret_cast<const u32x4v*>(st + r * 64 + uphys(r, c) * 16);
+            ca[i] = (uint32_t)(cur[i] >> sha);
+        }
+#pragma unroll
+        for (int j = 0; j < UTJ; j++) {
+            const int r = rb + 32 * j;
+            xb[j] = *reinterpret_cast<const u32x4v*>(st + USA + r * 64 + uphys(r, c) * 16);
+            cb[j] = (uint32_t)(cur[UTI + j] >> shb);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            typename UVec<KA>::type a[UTI];
+            typename UVec<KB>::type b[UTJ];
+#pragma unroll
+            for (int i = 0; i < UTI; i++)
+                a[i] = udecode<KA>(xa[i][q], uscale_bits<KA>(ugroup_code(ca[i], q, da.lg), da));
+#pragma unroll
+            for (int j = 0; j < UTJ; j++)
+                b[j] = udecode<KB>(xb[j][q], uscale_bits<KB>(ugroup_code(cb[j], q, db.lg), db));
+#pragma unroll
+            for (int i = 0; i < UTI; i++)
+#pragma unroll
+                for (int j = 0; j < UTJ; j++) {
+                    if constexpr (KA == DK_F16)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                }
+        }
+    }
+}
+
+template <bool CBF16, int KA, int KB>
+__global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_upcvt_lds(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, UDec da, UDec db, const float* ta, const float* tb, void* __restrict__ C,
+    int64_t M, int64_t N, int64_t K, int64_t ldc) {
+    static_assert((KA == DK_F16) == (KB == DK_F16), "the fp16 route needs both operands in fp16");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[UD * USTAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5, lrow = lane & 31;
+    const int wm = wave / UWGN, wn = wave % UWGN;
+    // XCD-aware grouped tile order
+    const int tm = (int)((M + UBM - 1) / UBM), tn = (int)((N + UBN - 1) / UBN);
+    const int T = tm * tn;
+    int bid = blockIdx.x;
+    if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+    constexpr int GM = 8;
+    const int group = bid / (GM * tn), first = group * GM;
+    const int gsz = (tm - first) < GM ? (tm - first) : GM;
+    const int in_g = bid - group * GM * tn;
+    const int64_t m0 = (int64_t)(first + in_g % gsz) * UBM, n0 = (int64_t)(in_g / gsz) * UBN;
+
+    const int rowb = (int)(K / 2), srowa = (int)(K >> da.lg), srowb = (int)(K >> db.lg);
+    const int64_t va = M - m0 < UBM ? M - m0 : UBM, vb = N - n0 < UBN ? N - n0 : UBN;
+    UPanels P;
+    P.a = ursrc(A + m0 * rowb, va * rowb);
+    P.b = ursrc(B + n0 * rowb, vb * rowb);
+    P.sa = ursrc(SA + m0 * srowa, va * srowa);
+    P.sb = ursrc(SB + n0 * srowb, vb * srowb);
+    P.z = ursrc(A, 0);
+    P.rowb = rowb;
+    P.srowa = srowa;
+    P.srowb = srowb;
+    P.spa = 128 >> da.lg;
+    P.spb = 128 >> db.lg;
+    P.nst = (int)(K / 128);
+
+    const int ra = wm * 32 * UTI + lrow, rb = wn * 32 * UTJ + lrow;
+    v16f acc[UTI][UTJ];
+#pragma unroll
+    for (int i = 0; i < UTI; i++)
+#pragma unroll
+        for (int j = 0; j < UTJ; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    uint64_t s0[UTI + UTJ], s1[UTI + UTJ];
+    ustage_dma(smem, P, 0, wave, lane);
+    ustage_scales(s0, P, 0, ra, rb);
+    ustage_dma(smem, P, 1, wave, lane);
+    for (int s = 0; s < P.nst; s += 2) {
+        ustep<KA, KB>(smem, P, s, wave, lane, half, ra, rb, da, db, acc, s0, s1);
+        if (s + 1 < P.nst) ustep<KA, KB>(smem, P, s + 1, wave, lane, half, ra, rb, da, db, acc, s1, s0);
+    }
+    uwait_vm<0>();
+
+    const float g = (ta ? *ta : 1.0f) * (tb ? *tb : 1.0f);
+#pragma unroll
+    for (int i = 0; i < UTI; i++)
+#pragma unroll
+        for (int j = 0; j < UTJ; j++) {
+            const int64_t n = n0 + wn * 32 * UTJ + 32 * j + lrow;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t m = m0 + wm * 32 * UTI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
+                if (m >= M) continue;
+                const float v = acc[i][j][r] * g;
+                if constexpr (CBF16) static_cast<uint16_t*>(C)[m * ldc + n] = bf16_rne(v);
+                else static_cast<float*>(C)[m * ldc + n] = v;
+            }
+        }
+}
+
+UDec udec(const UOperand& U) {
+    UDec d;
+    d.mul = U.kind == UK_UE5M3 ? 0x1p112f : 0x1p120f;
+    d.nan = U.kind == UK_UE5M3 ? 0xffu : 0x7fu;
+    d.lg = U.bc == 16 ? 4 : 5;
+    return d;
+}
+
+template <int KA, int KB>
+hipError_t launch_upcvt_lds_t(const UOperand& A, const UOperand& B, const float* ta, const float* tb, void* c,
+                              int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    const int64_t tiles = ((M + UBM - 1) / UBM) * ((N + UBN - 1) / UBN);
+    const UDec da = udec(A), db = udec(B);
+    if (c_bf16)
+        k_gemm_upcvt_lds<true, KA, KB><<<(unsigned)tiles, 64 * UNW, 0, s>>>(A.codes, A.scales, B.codes, B.scales, da,
+                                                                          db, ta, tb, c, M, N, K, ldc);
+    else
+        k_gemm_upcvt_lds<false, KA, KB><<<(unsigned)tiles, 64 * UNW, 0, s>>>(A.codes, A.scales, B.codes, B.scales, da,
+                                                                           db, ta, tb, c, M, N, K, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_upcvt_lds(const UOperand& A, const UOperand& B, const float* ta, const float* tb, void* c,
+                            int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    if (A.kind == UK_UE4M3 && B.kind == UK_UE4M3)
+        return launch_upcvt_lds_t<DK_F16, DK_F16>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+    const bool pa = A.kind == UK_E8M0, pb = B.kind == UK_E8M0;
+    if (pa && pb) return launch_upcvt_lds_t<DK_E8M0, DK_E8M0>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+    if (pa) return launch_upcvt_lds_t<DK_E8M0, DK_FP8>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+    if (pb) return launch_upcvt_lds_t<DK_FP8, DK_E8M0>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+    return launch_upcvt_lds_t<DK_FP8, DK_FP8>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+}
+
 }  // namespace
 
 bool gemm_upcvt_scale_ok(int scale) {
@@ -179,6 +483,8 @@ hipError_t launch_gemm_upcvt(int sca, int bca, const uint8_t* a, const uint8_t* 
         return hipErrorInvalidValue;
     const UOperand A = {a, sa, ukind(sca), bca};
     const UOperand B = {b, sb, ukind(scb), bcb};
+    if (K % 128 == 0 && (bca == 16 || bca == 32) && (bcb == 16 || bcb == 32))
+        return launch_upcvt_lds(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
     dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
     if (c_bf16) k_gemm_upcvt<true><<<grid, 256, 0, s>>>(A, B, ta, tb, c, M, N, K, ldc);
     else k_gemm_upcvt<false><<<grid, 256, 0, s>>>(A, B, ta, tb, c, M, N, K, ldc);

@@ -324,8 +324,12 @@ def test_upcvt_exact_case(ka, kb, M, N, K):
 
 
 @pytest.mark.parametrize("ka,kb", UPC_PAIRS)
-@pytest.mark.parametrize("M,N,K", [(257, 130, 1024), (64, 96, 352)])
+@pytest.mark.parametrize("M,N,K", [(257, 130, 1024), (64, 96, 352), (520, 1030, 512), (512, 1024, 384)])
 def test_upcvt_random_scales(ka, kb, M, N, K):
+    """Random block scales: within fp32 accumulation error of the oracle's
+    fp64 product.  The shapes take both kernels: K a multiple of 128 with
+    1 x 16 or 1 x 32 blocks the LDS-staged one (several ragged tiles; an odd
+    stage count; a tile count that is a multiple of 8), else the register one."""
     if K % UPC[ka][1] or K % UPC[kb][1]:
         pytest.skip("K is not a whole number of blocks")
     rng = np.random.default_rng(K + 7)
