@@ -12,8 +12,10 @@
 // permuted by a row-dependent rotation (FP6) or XOR (E2M1) so that the chunk
 // reads of 16 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
 // codes, 24 bytes) spans one whole chunk and half of the next: two 16-byte
-// reads, put in order per lane.  The scales of a stage (4
-// bytes per row) are one dword load per row tile, a stage ahead.
+// reads, put in order per lane.  The scales of a stage (4 bytes per row) come
+// with its codes, a dword per lane, so that the only loads in flight in the
+// loop are the DMA the stage waits count (and, with macro-block scales, one
+// byte per operand row a stage ahead).
 #include "mx_kernels.hpp"
 
 namespace mxk {
@@ -59,12 +61,15 @@ struct LGeo {
     // macro block): each lane loads the bytes of its operand rows with the
     // stage's E8M0 scales; A's go through LDS (BM bytes after the codes) to
     // the lanes that hold those rows' accumulators
-    static constexpr int NS = (TI + TJ) * (MBS ? 2 : 1);   // scale registers per stage
-    static constexpr int OFF_M = SA + SB;
+    static constexpr int NS = MBS ? TI + TJ : 1;       // macro scale registers per stage
+    static constexpr int OFF_S = SA + SB;              // the stage's block scales, A rows then B rows
+    static constexpr int OFF_M = OFF_S + (BM + BN) * 4;
     static constexpr int STAGE = OFF_M + ((MBS & 1) ? BM : 0);
     static constexpr int PA = SA / 1024, PB = SB / 1024;
-    static constexpr int PW = (PA + PB) / NW;          // DMA pieces per wave per stage
-    static_assert((PA + PB) % NW == 0, "DMA pieces split evenly over the waves");
+    static constexpr int PW = (PA + PB) / NW;          // code DMA pieces per wave per stage
+    static constexpr int SPW = (BM + BN) / 64 / NW;    // scale DMA pieces (a row per lane) per wave
+    static_assert((PA + PB) % NW == 0 && (BM + BN) % (64 * NW) == 0, "DMA pieces split evenly over the waves");
+    static_assert((BM / 64) % SPW == 0, "a wave's scale pieces lie in one operand");
 };
 
 __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -129,8 +134,11 @@ struct LPanels {
 
 // DMA of stage s into its ring slot; stages past K go through the zero-size
 // resource (no memory access), so every stage issues the same count.  Piece g
-// of an operand covers 64 consecutive 16-byte LDS slots; the lane writing slot
-// (row r, physical chunk q) fetches the logical chunk stored there.
+// of the codes covers 64 consecutive 16-byte LDS slots; the lane writing slot
+// (row r, physical chunk q) fetches the logical chunk stored there.  Then the
+// stage's scale dword of each tile row.  The operand of a piece is a select,
+// not a branch: with no branch around the loads the compiler's own counts of
+// loads in flight stay exact, and it never waits for a stage still in flight.
 template <class G>
 __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s, int wave, int lane) {
 
@@ -141,45 +149,45 @@ __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s
     using OB = Op<G::FB>;
     uint8_t* slot = smem + (s % G::D) * G::STAGE;
     const bool in = s < P.nst;
+    const rsrc_t pa = P.a, pb = P.b, psa = P.sa, psb = P.sb, pz = P.z;
+    const int rowa = (int)P.rowa, rowb = (int)P.rowb;
 #pragma unroll
     for (int k = 0; k < G::PW; k++) {
         const int g = wave * G::PW + k;                   // uniform
-        if (g < G::PA) {
-            const int f = g * 64 + lane, r = f / OA::C, q = f % OA::C;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.a : P.z, (lds_void*)(slot + g * 1024), 16,
-                                                     (int)(r * P.rowa) + OA::logical(r, q) * 16, s * OA::R, 0, 0);
-        } else {
-            const int h = g - G::PA;
-            const int f = h * 64 + lane, r = f / OB::C, q = f % OB::C;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.b : P.z, (lds_void*)(slot + G::SA + h * 1024), 16,
-                                                     (int)(r * P.rowb) + OB::logical(r, q) * 16, s * OB::R, 0, 0);
-        }
+        const bool isb = g >= G::PA;
+        const int f = (isb ? g - G::PA : g) * 64 + lane;
+        const int ra = f / OA::C, rb = f / OB::C;
+        const int va = ra * rowa + OA::logical(ra, f % OA::C) * 16;
+        const int vb = rb * rowb + OB::logical(rb, f % OB::C) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? pb : pa) : pz, (lds_void*)(slot + g * 1024), 16,
+                                                 isb ? vb : va, s * (isb ? OB::R : OA::R), 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < G::SPW; k++) {
+        const int g = wave * G::SPW + k;                  // uniform
+        const bool isb = g >= G::BM / 64;
+        const int row = (isb ? g - G::BM / 64 : g) * 64 + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? psb : psa) : pz, (lds_void*)(slot + G::OFF_S + g * 256),
+                                                 4, row * P.kblocks, 4 * s, 0, 0);
     }
 #endif
 }
 
-// the 4 scale bytes of stage s for this lane's row tiles (A: TI, then B:
-// TJ), then (MBS) the macro scale byte of each of those rows
+// (MBS) the macro scale byte of stage s of each of this lane's operand rows
+// (A: TI, then B: TJ), a stage ahead
 template <class G>
-__device__ __forceinline__ void stage_scales(uint32_t (&o)[G::NS], const LPanels& P, int s, int ra, int rb) {
-    const bool in = s < P.nst;
-#pragma unroll
-    for (int i = 0; i < G::TI; i++)
-        o[i] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sa : P.z, (ra + 32 * i) * P.kblocks + 4 * s, 0, 0);
-#pragma unroll
-    for (int j = 0; j < G::TJ; j++)
-        o[G::TI + j] = __builtin_amdgcn_raw_buffer_load_b32(in ? P.sb : P.z, (rb + 32 * j) * P.kblocks + 4 * s, 0, 0);
+__device__ __forceinline__ void stage_macro(uint32_t (&o)[G::NS], const LPanels& P, int s, int ra, int rb) {
     if constexpr (G::MBS != 0) {
-        constexpr int B0 = G::TI + G::TJ;
+        const bool in = s < P.nst;
+        const rsrc_t pma = P.ma, pmb = P.mb, pz = P.z;
 #pragma unroll
         for (int i = 0; i < G::TI; i++)
-            o[B0 + i] = (G::MBS & 1) ? __builtin_amdgcn_raw_buffer_load_b8(in ? P.ma : P.z, (ra + 32 * i) * P.mcols + s, 0, 0)
-                                     : 0x38u;
+            o[i] = (G::MBS & 1) ? __builtin_amdgcn_raw_buffer_load_b8(in ? pma : pz, (ra + 32 * i) * P.mcols + s, 0, 0)
+                                : 0x38u;
 #pragma unroll
         for (int j = 0; j < G::TJ; j++)
-            o[B0 + G::TI + j] =
-                (G::MBS & 2) ? __builtin_amdgcn_raw_buffer_load_b8(in ? P.mb : P.z, (rb + 32 * j) * P.mcols + s, 0, 0)
-                             : 0x38u;
+            o[G::TI + j] = (G::MBS & 2) ? __builtin_amdgcn_raw_buffer_load_b8(in ? pmb : pz, (rb + 32 * j) * P.mcols + s, 0, 0)
+                                        : 0x38u;
     }
 }
 
@@ -198,29 +206,36 @@ __device__ __forceinline__ void wait_vm() {
 // barrier publishes was waited for with wait_vm)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// one stage: wait for its DMA and scales, free the slot two ahead, issue the
-// next stage's scales and the DMA two stages ahead, multiply
+// one stage: wait for its DMA (codes and scales), free the slot two ahead,
+// issue the next stage's macro scales and the DMA two stages ahead, multiply
 template <class G>
 __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s, int wave, int lane, int half, int ra,
                                          int rb, v16f (&acc)[G::TI][G::TJ], const uint32_t (&cur)[G::NS],
                                          uint32_t (&nxt)[G::NS]) {
-    wait_vm<G::PW>();
+    wait_vm<G::PW + G::SPW>();
     if constexpr ((G::MBS & 1) != 0) {
         // A's macro bytes of stage s to LDS for the accumulator rows (waves
         // that share A rows write the same values)
         uint8_t* ms = smem + (s % G::D) * G::STAGE + G::OFF_M;
 #pragma unroll
-        for (int i = 0; i < G::TI; i++) ms[ra + 32 * i] = (uint8_t)cur[G::TI + G::TJ + i];
+        for (int i = 0; i < G::TI; i++) ms[ra + 32 * i] = (uint8_t)cur[i];
     }
     // every wave's share of stage s has landed and every wave is done
     // reading slot (s + 2) % 3 (stage s - 1)
     lds_barrier();
-    stage_scales<G>(nxt, P, s + 1, ra, rb);
+    stage_macro<G>(nxt, P, s + 1, ra, rb);
     stage_dma<G>(smem, P, s + 2, wave, lane);
     const uint8_t* st = smem + (s % G::D) * G::STAGE;
+    // this lane's scale bytes: byte 2T of the row's dword after the shift by
+    // 8 * half serves substep T
     int sc[G::TI + G::TJ];
 #pragma unroll
-    for (int i = 0; i < G::TI + G::TJ; i++) sc[i] = (int)(cur[i] >> (8 * half));
+    for (int i = 0; i < G::TI; i++)
+        sc[i] = (int)(*reinterpret_cast<const uint32_t*>(st + G::OFF_S + (ra + 32 * i) * 4) >> (8 * half));
+#pragma unroll
+    for (int j = 0; j < G::TJ; j++)
+        sc[G::TI + j] =
+            (int)(*reinterpret_cast<const uint32_t*>(st + G::OFF_S + (G::BM + rb + 32 * j) * 4) >> (8 * half));
     if constexpr (G::MBS == 0) {
         substep<0, G>(acc, st, ra, rb, half, sc);
         substep<1, G>(acc, st, ra, rb, half, sc);
@@ -240,7 +255,7 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
         const uint8_t* ms = st + G::OFF_M;
         float fb[G::TJ];
 #pragma unroll
-        for (int j = 0; j < G::TJ; j++) fb[j] = ue4m3(cur[2 * G::TI + G::TJ + j]);
+        for (int j = 0; j < G::TJ; j++) fb[j] = ue4m3(cur[G::TI + j]);
 #pragma unroll
         for (int i = 0; i < G::TI; i++) {
             // accumulator register 4q + p holds row 8q + 4 half + p of the tile
@@ -267,7 +282,7 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc,
     const uint8_t* __restrict__ MA, const uint8_t* __restrict__ MB) {
     constexpr int FA = G::FA, FB = G::FB, TI = G::TI, TJ = G::TJ, D = G::D;
-    static_assert(G::PW + G::NS <= 63, "vmcnt");
+    static_assert(2 * (G::PW + G::SPW) + G::NS <= 63, "vmcnt");
     static_assert(D * G::STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
     const int lane = threadIdx.x & 63;
@@ -308,13 +323,16 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    uint32_t s0[G::NS], s1[G::NS];
+    uint32_t mc[G::NS], mn[G::NS];
+#pragma unroll
+    for (int i = 0; i < G::NS; i++) mc[i] = mn[i] = 0x38u;
     stage_dma<G>(smem, P, 0, wave, lane);
-    stage_scales<G>(s0, P, 0, ra, rb);
+    stage_macro<G>(mc, P, 0, ra, rb);
     stage_dma<G>(smem, P, 1, wave, lane);
-    for (int s = 0; s < nst; s += 2) {
-        lds_step<G>(smem, P, s, wave, lane, half, ra, rb, acc, s0, s1);
-        if (s + 1 < nst) lds_step<G>(smem, P, s + 1, wave, lane, half, ra, rb, acc, s1, s0);
+    for (int s = 0; s < nst; s++) {
+        lds_step<G>(smem, P, s, wave, lane, half, ra, rb, acc, mc, mn);
+#pragma unroll
+        for (int i = 0; i < G::NS; i++) mc[i] = mn[i];
     }
     wait_vm<0>();
 

@@ -172,10 +172,10 @@ int ukind(int scale) { return scale == SC_E8M0 ? UK_E8M0 : scale == SC_UE5M3 ? U
 // 256 tiles of 8 waves (4 x 2 MFMA tiles each), 128-wide K stages of codes (64
 // bytes per row, four 16-byte chunks XOR-permuted per row so the chunk reads
 // of 16 consecutive rows hit distinct banks) in a three-deep LDS ring filled
-// by LDS-DMA two stages ahead; the stage's block scales (8 bytes per row at
-// most) are one load per row tile, a stage ahead.  Each lane decodes its
-// 32-code chunk group by group, without branches, and feeds the instruction
-// right away.
+// by LDS-DMA two stages ahead, together with the stage's block scales (8
+// bytes per row at most), so no load in the loop writes registers.  Each
+// lane decodes its 32-code chunk group by group, without branches, and feeds
+// the instruction right away.
 //
 // Two routes.  When both operands carry UE4M3 scales (NVFP4, with or without
 // its tensor scale) every product q * s has at most five significant bits and
@@ -195,8 +195,10 @@ typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 constexpr int UWGM = 2, UWGN = 4, UTI = 4, UTJ = 2, UNW = UWGM * UWGN;
 constexpr int UBM = UWGM * 32 * UTI, UBN = UWGN * 32 * UTJ, UD = 3;
-constexpr int USA = UBM * 64, USTAGE = (UBM + UBN) * 64;
-constexpr int UPW = USTAGE / 1024 / UNW;               // DMA pieces per wave per stage
+constexpr int USA = UBM * 64, UCODES = (UBM + UBN) * 64;   // A codes, then B codes
+constexpr int USTAGE = UCODES + (UBM + UBN) * 8;           // then 8 scale bytes per row
+constexpr int UPW = UCODES / 1024 / UNW;               // code DMA pieces per wave per stage
+constexpr int USW = (UBM + UBN) * 2 / 64 / UNW;        // scale DMA pieces (a dword per lane) per wave
 
 // operand decode kinds of the LDS kernel
 enum { DK_E8M0 = 0, DK_FP8 = 1, DK_F16 = 2 };
@@ -226,41 +228,47 @@ __device__ __forceinline__ void uwait_vm() {
 __device__ __forceinline__ void ubarrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // DMA of stage s (device pass only: the host pass rejects the LDS-DMA builtin
-// in a template and would drop the launch stubs)
+// in a template and would drop the launch stubs): the codes in 16-byte pieces,
+// then each row's stage scales, 8 bytes (1 x 32 blocks: 4, twice) a dword per
+// lane.  A wave's pieces
+// all fall in one operand's panel, so the panel is a select, not a branch, and
+// every wave issues the same UPW + USW loads per stage, oldest first, which the
+// stage waits count on.
+static_assert((USA / 1024) % UPW == 0 && (UBM * 2 / 64) % USW == 0,
+              "a wave's DMA pieces must not straddle the two panels");
 __device__ __forceinline__ void ustage_dma(uint8_t* smem, const UPanels& P, int s, int wave, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    uint8_t* slot = smem + (s % UD) * USTAGE;
+    const rsrc_t pa = P.a, pb = P.b, psa = P.sa, psb = P.sb, pz = P.z;
     const bool in = s < P.nst;
+    uint8_t* slot = smem + (s % UD) * USTAGE;
+    {
+        const bool isb = wave * UPW >= USA / 1024;           // uniform
+        const rsrc_t r = in ? (isb ? pb : pa) : pz;
+        const int h0 = isb ? wave * UPW - USA / 1024 : wave * UPW;
+        uint8_t* base = slot + (isb ? USA : 0);
 #pragma unroll
-    for (int k = 0; k < UPW; k++) {
-        const int g = wave * UPW + k;                    // uniform
-        if (g < USA / 1024) {
-            const int f = g * 64 + lane, r = f >> 2, q = f & 3;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.a : P.z, (lds_void*)(slot + g * 1024), 16,
-                                                     r * P.rowb + uphys(r, q) * 16, s * 64, 0, 0);
-        } else {
-            const int h = g - USA / 1024;
-            const int f = h * 64 + lane, r = f >> 2, q = f & 3;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? P.b : P.z, (lds_void*)(slot + USA + h * 1024), 16,
-                                                     r * P.rowb + uphys(r, q) * 16, s * 64, 0, 0);
+        for (int k = 0; k < UPW; k++) {
+            const int f = (h0 + k) * 64 + lane, row = f >> 2, q = f & 3;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(base + (h0 + k) * 1024), 16,
+                                                     row * P.rowb + uphys(row, q) * 16, s * 64, 0, 0);
+        }
+    }
+    {
+        const bool isb = wave * USW >= UBM * 2 / 64;          // uniform
+        const rsrc_t r = in ? (isb ? psb : psa) : pz;
+        const int h0 = isb ? wave * USW - UBM * 2 / 64 : wave * USW;
+        const int srow = isb ? P.srowb : P.srowa, sp = isb ? P.spb : P.spa;
+        uint8_t* base = slot + UCODES + (isb ? UBM * 8 : 0);
+#pragma unroll
+        for (int k = 0; k < USW; k++) {
+            // 1 x 32 blocks: the second dword repeats the first, so that no
+            // load reaches past the row's last stage
+            const int f = (h0 + k) * 64 + lane, row = f >> 1, d = sp == 8 ? f & 1 : 0;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(base + (h0 + k) * 256), 4, row * srow + 4 * d,
+                                                     sp * s, 0, 0);
         }
     }
 #endif
-}
-
-// the block scales of stage s for this lane's rows (8 bytes for 1 x 16
-// blocks, 4 for 1 x 32), A's row tiles then B's
-__device__ __forceinline__ uint64_t urow_scales(rsrc_t r, int off, int sp) {
-    if (sp == 8) return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ void ustage_scales(uint64_t (&o)[UTI + UTJ], const UPanels& P, int s, int ra, int rb) {
-    const bool in = s < P.nst;
-#pragma unroll
-    for (int i = 0; i < UTI; i++) o[i] = urow_scales(in ? P.sa : P.z, (ra + 32 * i) * P.srowa + P.spa * s, P.spa);
-#pragma unroll
-    for (int j = 0; j < UTJ; j++)
-        o[UTI + j] = urow_scales(in ? P.sb : P.z, (rb + 32 * j) * P.srowb + P.spb * s, P.spb);
 }
 
 // eight fp16 products q * s of the codes in dword w; h holds s * 2^-8 twice
@@ -314,31 +322,32 @@ __device__ __forceinline__ uint32_t ugroup_code(uint32_t x, int q, int lg) {
 
 template <int KA, int KB>
 __device__ __forceinline__ void ustep(uint8_t* smem, const UPanels& P, int s, int wave, int lane, int half, int ra,
-                                      int rb, const UDec& da, const UDec& db, v16f (&acc)[UTI][UTJ],
-                                      const uint64_t (&cur)[UTI + UTJ], uint64_t (&nxt)[UTI + UTJ]) {
-    uwait_vm<UPW>();
+                                      int rb, const UDec& da, const UDec& db, v16f (&acc)[UTI][UTJ]) {
+    uwait_vm<UPW + USW>();
     ubarrier();
-    ustage_scales(nxt, P, s + 1, ra, rb);
     ustage_dma(smem, P, s + 2, wave, lane);
     const uint8_t* st = smem + (s % UD) * USTAGE;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
         const int c = 2 * t + half;
-        // first scale byte of chunk c: block (32 c) >> lg of the stage
-        const int sha = 8 * ((32 * c) >> da.lg), shb = 8 * ((32 * c) >> db.lg);
+        // the dword of each row's stage scales that holds chunk c's (1 x 16
+        // blocks: bytes 2c, 2c + 1, in dword t; 1 x 32: byte c, in dword 0),
+        // shifted to put them at the bottom
+        const int oa = da.lg == 4 ? 4 * t : 0, ob = db.lg == 4 ? 4 * t : 0;
+        const int sha = da.lg == 4 ? 16 * half : 8 * c, shb = db.lg == 4 ? 16 * half : 8 * c;
         u32x4v xa[UTI], xb[UTJ];
         uint32_t ca[UTI], cb[UTJ];
 #pragma unroll
         for (int i = 0; i < UTI; i++) {
             const int r = ra + 32 * i;
             xa[i] = *reinterpret_cast<const u32x4v*>(st + r * 64 + uphys(r, c) * 16);
-            ca[i] = (uint32_t)(cur[i] >> sha);
+            ca[i] = *reinterpret_cast<const uint32_t*>(st + UCODES + r * 8 + oa) >> sha;
         }
 #pragma unroll
         for (int j = 0; j < UTJ; j++) {
             const int r = rb + 32 * j;
             xb[j] = *reinterpret_cast<const u32x4v*>(st + USA + r * 64 + uphys(r, c) * 16);
-            cb[j] = (uint32_t)(cur[UTI + j] >> shb);
+            cb[j] = *reinterpret_cast<const uint32_t*>(st + UCODES + (UBM + r) * 8 + ob) >> shb;
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
@@ -408,14 +417,9 @@ __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int j = 0; j < UTJ; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-    uint64_t s0[UTI + UTJ], s1[UTI + UTJ];
     ustage_dma(smem, P, 0, wave, lane);
-    ustage_scales(s0, P, 0, ra, rb);
     ustage_dma(smem, P, 1, wave, lane);
-    for (int s = 0; s < P.nst; s += 2) {
-        ustep<KA, KB>(smem, P, s, wave, lane, half, ra, rb, da, db, acc, s0, s1);
-        if (s + 1 < P.nst) ustep<KA, KB>(smem, P, s + 1, wave, lane, half, ra, rb, da, db, acc, s1, s0);
-    }
+    for (int s = 0; s < P.nst; s++) ustep<KA, KB>(smem, P, s, wave, lane, half, ra, rb, da, db, acc);
     uwait_vm<0>();
 
     const float g = (ta ? *ta : 1.0f) * (tb ? *tb : 1.0f);
