@@ -8,19 +8,22 @@
 // K-values of a lane, so a 16-element block with a 4-bit-significand scale
 // has no exact mapping onto it (an E2M1 value times such a scale needs up to
 // six significant bits, beyond FP8, FP6 and FP4).  Here each lane decodes its
-// codes to fp32, multiplies by the block scale and narrows to bf16 -- exactly,
-// since the product has at most six significant bits -- and the bf16 products
-// run on V_MFMA_F32_32X32X16_BF16.  (The scaled converts use only the exponent
-// of their scale operand, so they apply E8M0 scales directly but not UE4M3 /
-// UE5M3 ones: measured on gfx950.)
-// The per-tensor scales multiply the fp32 result once at the end.
+// codes, multiplies by the block scale -- exactly, since the product has at
+// most six significant bits -- and the products run on the fp16 or bf16
+// matrix instruction.  (The scaled converts use only the exponent of their
+// scale operand, so they apply E8M0 scales directly but not UE4M3 / UE5M3
+// ones: measured on gfx950.)  The per-tensor scales multiply the fp32 result
+// once at the end.
 //
-// Layout: a lane of the bf16 instruction supplies 8 K-values of its row.  The
-// K order inside one instruction is free as long as A and B agree, so lane
-// (row r, half h) takes K = k0 + 32 h + 8 j + (0..7) in the j-th of the four
-// instructions of a 64-wide K step: the 16 code bytes of k0 + 32 h .. + 31,
-// one load, and every group of 8 lies inside one block (blocks are multiples
-// of 8 wide).
+// Two kernels: an LDS-staged one (1 x 16 and 1 x 32 blocks, K a multiple of
+// 128; below) and a register-only one for the rest.
+//
+// Layout of the register-only kernel: a lane of the bf16 instruction supplies
+// 8 K-values of its row.  The K order inside one instruction is free as long
+// as A and B agree, so lane (row r, half h) takes K = k0 + 32 h + 8 j + (0..7)
+// in the j-th of the four instructions of a 64-wide K step: the 16 code bytes
+// of k0 + 32 h .. + 31, one load, and every group of 8 lies inside one block
+// (blocks are multiples of 8 wide).
 #include <type_traits>
 
 #include "mx_kernels.hpp"
@@ -178,7 +181,7 @@ int ukind(int scale) { return scale == SC_E8M0 ? UK_E8M0 : scale == SC_UE5M3 ? U
 // the instruction right away.
 //
 // Two routes.  When both operands carry UE4M3 scales (NVFP4, with or without
-// its tensor scale) every product q * s has at most five significant bits and
+// its tensor scale) every product q * s has at most six significant bits and
 // lies in [2^-10, 2688]: exact in fp16, so the codes are decoded to fp16 (the
 // convert scaled by 2^8, times the scale code shifted into an fp16 bit pattern,
 // which is s * 2^-8) and multiplied by the fp16 instruction at the bf16 rate,
