@@ -12,10 +12,11 @@
 // permuted by a row-dependent rotation (FP6) or XOR (E2M1) so that the chunk
 // reads of 16 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
 // codes, 24 bytes) spans one whole chunk and half of the next: two 16-byte
-// reads, put in order per lane.  The scales of a stage (4 bytes per row) come
-// with its codes, a dword per lane, so that the only loads in flight in the
-// loop are the DMA the stage waits count (and, with macro-block scales, one
-// byte per operand row a stage ahead).
+// reads, put in order per lane.  The block scales (4 bytes per row and stage)
+// come by LDS-DMA too, in groups of 4 stages (16 bytes of a row per lane: a
+// quarter of the L2 requests of a dword per stage), so that the only loads in
+// flight in the loop are the DMA the stage waits count (and, with macro-block
+// scales, one byte per operand row a stage ahead).
 #include "mx_kernels.hpp"
 
 namespace mxk {
@@ -51,7 +52,7 @@ struct Op {
     }
 };
 
-template <int FA_, int FB_, int WGM_, int WGN_, int TI_, int TJ_, int MBS_ = 0>
+template <int FA_, int FB_, int WGM_, int WGN_, int TI_, int TJ_, int MBS_ = 0, int SG_ = 4>
 struct LGeo {
     static constexpr int FA = FA_, FB = FB_, MBS = MBS_;
     static constexpr int WGM = WGM_, WGN = WGN_, TI = TI_, TJ = TJ_;   // waves, MFMA tiles per wave
@@ -62,14 +63,23 @@ struct LGeo {
     // stage's E8M0 scales; A's go through LDS (BM bytes after the codes) to
     // the lanes that hold those rows' accumulators
     static constexpr int NS = MBS ? TI + TJ : 1;       // macro scale registers per stage
-    static constexpr int OFF_S = SA + SB;              // the stage's block scales, A rows then B rows
-    static constexpr int OFF_M = OFF_S + (BM + BN) * 4;
+    static constexpr int OFF_M = SA + SB;
     static constexpr int STAGE = OFF_M + ((MBS & 1) ? BM : 0);
     static constexpr int PA = SA / 1024, PB = SB / 1024;
     static constexpr int PW = (PA + PB) / NW;          // code DMA pieces per wave per stage
-    static constexpr int SPW = (BM + BN) / 64 / NW;    // scale DMA pieces (a row per lane) per wave
+    // block scales travel in groups of SG stages, the 4 SG bytes of a row per
+    // lane, into NB buffers after the ring: groups of 4 stages (K >= 512) one
+    // group ahead in two buffers, or single stages two ahead in three
+    static constexpr int SG = SG_;
+    static constexpr int NB = SG == 1 ? 3 : 2;
+    static constexpr int GROW = 4 * SG;
+    static constexpr int GBUF = (BM + BN) * GROW;
+    static constexpr int OFF_G = D * STAGE;
+    static constexpr int SMEM = OFF_G + NB * GBUF;
+    static_assert(SG == 1 || SG == 4, "scale groups of 1 or 4 stages");
+    static constexpr int GPW = (BM + BN) / 64 / NW;    // group DMA pieces per wave
     static_assert((PA + PB) % NW == 0 && (BM + BN) % (64 * NW) == 0, "DMA pieces split evenly over the waves");
-    static_assert((BM / 64) % SPW == 0, "a wave's scale pieces lie in one operand");
+    static_assert((BM / 64) % GPW == 0, "a wave's scale pieces lie in one operand");
 };
 
 __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -149,7 +159,7 @@ __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s
     using OB = Op<G::FB>;
     uint8_t* slot = smem + (s % G::D) * G::STAGE;
     const bool in = s < P.nst;
-    const rsrc_t pa = P.a, pb = P.b, psa = P.sa, psb = P.sb, pz = P.z;
+    const rsrc_t pa = P.a, pb = P.b, pz = P.z;
     const int rowa = (int)P.rowa, rowb = (int)P.rowb;
 #pragma unroll
     for (int k = 0; k < G::PW; k++) {
@@ -162,13 +172,36 @@ __device__ __forceinline__ void stage_dma(uint8_t* smem, const LPanels& P, int s
         __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? pb : pa) : pz, (lds_void*)(slot + g * 1024), 16,
                                                  isb ? vb : va, s * (isb ? OB::R : OA::R), 0, 0);
     }
+#endif
+}
+
+// first scale byte of group g that its buffer holds: groups of 4 stages
+// start 16 g into the row, except a partial last group, which is read as the
+// row's last 16 bytes so that no load reaches past the row (the panel's last
+// row ends at the resource bound)
+template <class G>
+__device__ __forceinline__ int group_start(int g, int kblocks) {
+    if constexpr (G::SG == 1) return 4 * g;
+    else return 16 * g < kblocks - 16 ? 16 * g : kblocks - 16;
+}
+
+// DMA of scale group g (stages SG g .. SG g + SG - 1) into its buffer: one
+// row's 4 SG bytes per lane.  Groups past K read through the zero-size
+// resource.
+template <class G>
+__device__ __forceinline__ void group_dma(uint8_t* smem, const LPanels& P, int g, int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const rsrc_t psa = P.sa, psb = P.sb, pz = P.z;
+    const bool in = g * G::SG < P.nst;
+    uint8_t* buf = smem + G::OFF_G + (g % G::NB) * G::GBUF;
+    const int start = group_start<G>(g, P.kblocks);
 #pragma unroll
-    for (int k = 0; k < G::SPW; k++) {
-        const int g = wave * G::SPW + k;                  // uniform
-        const bool isb = g >= G::BM / 64;
-        const int row = (isb ? g - G::BM / 64 : g) * 64 + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? psb : psa) : pz, (lds_void*)(slot + G::OFF_S + g * 256),
-                                                 4, row * P.kblocks, 4 * s, 0, 0);
+    for (int k = 0; k < G::GPW; k++) {
+        const int q = wave * G::GPW + k;                  // uniform
+        const bool isb = q >= G::BM / 64;
+        const int row = (isb ? q - G::BM / 64 : q) * 64 + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? psb : psa) : pz, (lds_void*)(buf + q * 64 * G::GROW),
+                                                 G::GROW, row * P.kblocks + start, 0, 0, 0);
     }
 #endif
 }
@@ -212,7 +245,11 @@ template <class G>
 __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s, int wave, int lane, int half, int ra,
                                          int rb, v16f (&acc)[G::TI][G::TJ], const uint32_t (&cur)[G::NS],
                                          uint32_t (&nxt)[G::NS]) {
-    wait_vm<G::PW + G::SPW>();
+    // in flight after stage s's codes: the codes of s + 1, and a scale group
+    // if stage s - 1 issued one after them (every stage with single-stage
+    // groups, whose prologue issues groups 0 and 1 in the same order)
+    if (G::SG == 1 || (s & (G::SG - 1)) == 1) wait_vm<G::PW + G::GPW>();
+    else wait_vm<G::PW>();
     if constexpr ((G::MBS & 1) != 0) {
         // A's macro bytes of stage s to LDS for the accumulator rows (waves
         // that share A rows write the same values)
@@ -225,17 +262,23 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
     lds_barrier();
     stage_macro<G>(nxt, P, s + 1, ra, rb);
     stage_dma<G>(smem, P, s + 2, wave, lane);
+    // the next scale group into the buffer of a group every wave has finished
+    // reading (before the barrier above): 4-stage groups one ahead, single
+    // stages two ahead
+    if constexpr (G::SG == 1) group_dma<G>(smem, P, s + 2, wave, lane);
+    else if ((s & (G::SG - 1)) == 0) group_dma<G>(smem, P, s / G::SG + 1, wave, lane);
     const uint8_t* st = smem + (s % G::D) * G::STAGE;
-    // this lane's scale bytes: byte 2T of the row's dword after the shift by
-    // 8 * half serves substep T
+    // this lane's scale bytes: byte 2T of the row's stage dword after the
+    // shift by 8 * half serves substep T
+    const int grp = s / G::SG;
+    const uint8_t* gs = smem + G::OFF_G + (grp % G::NB) * G::GBUF + 4 * s - group_start<G>(grp, P.kblocks);
     int sc[G::TI + G::TJ];
 #pragma unroll
     for (int i = 0; i < G::TI; i++)
-        sc[i] = (int)(*reinterpret_cast<const uint32_t*>(st + G::OFF_S + (ra + 32 * i) * 4) >> (8 * half));
+        sc[i] = (int)(*reinterpret_cast<const uint32_t*>(gs + (ra + 32 * i) * G::GROW) >> (8 * half));
 #pragma unroll
     for (int j = 0; j < G::TJ; j++)
-        sc[G::TI + j] =
-            (int)(*reinterpret_cast<const uint32_t*>(st + G::OFF_S + (G::BM + rb + 32 * j) * 4) >> (8 * half));
+        sc[G::TI + j] = (int)(*reinterpret_cast<const uint32_t*>(gs + (G::BM + rb + 32 * j) * G::GROW) >> (8 * half));
     if constexpr (G::MBS == 0) {
         substep<0, G>(acc, st, ra, rb, half, sc);
         substep<1, G>(acc, st, ra, rb, half, sc);
@@ -282,9 +325,9 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t ldc,
     const uint8_t* __restrict__ MA, const uint8_t* __restrict__ MB) {
     constexpr int FA = G::FA, FB = G::FB, TI = G::TI, TJ = G::TJ, D = G::D;
-    static_assert(2 * (G::PW + G::SPW) + G::NS <= 63, "vmcnt");
-    static_assert(D * G::STAGE <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[D * G::STAGE];
+    static_assert(2 * G::PW + G::GPW + G::NS <= 63, "vmcnt");
+    static_assert(G::SMEM <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, lrow = lane & 31;
@@ -327,8 +370,10 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int i = 0; i < G::NS; i++) mc[i] = mn[i] = 0x38u;
     stage_dma<G>(smem, P, 0, wave, lane);
+    group_dma<G>(smem, P, 0, wave, lane);
     stage_macro<G>(mc, P, 0, ra, rb);
     stage_dma<G>(smem, P, 1, wave, lane);
+    if constexpr (G::SG == 1) group_dma<G>(smem, P, 1, wave, lane);
     for (int s = 0; s < nst; s++) {
         lds_step<G>(smem, P, s, wave, lane, half, ra, rb, acc, mc, mn);
 #pragma unroll
@@ -359,14 +404,25 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
 #define LDS_TJ 2
 #endif
 
+template <class G>
+hipError_t launch_lds_g(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c, int64_t M,
+                        int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s, const uint8_t* ma,
+                        const uint8_t* mb) {
+    const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
+    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
+    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
+    return hipGetLastError();
+}
+
+// scale groups of 4 stages need K >= 512 (a whole group fits a scale row)
 template <int FA, int FB>
 hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c, int64_t M,
                         int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
-    using G = LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ>;
-    const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
-    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, nullptr, nullptr);
-    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, nullptr, nullptr);
-    return hipGetLastError();
+    if (K >= 512)
+        return launch_lds_g<LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ, 0, 4>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16,
+                                                                               s, nullptr, nullptr);
+    return launch_lds_g<LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ, 0, 1>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s,
+                                                                           nullptr, nullptr);
 }
 
 // MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): 128 x 128
@@ -376,11 +432,9 @@ template <int MBS>
 hipError_t launch_lds_mbs_t(const uint8_t* a, const uint8_t* sa, const uint8_t* ma, const uint8_t* b,
                             const uint8_t* sb, const uint8_t* mb, void* c, int64_t M, int64_t N, int64_t K,
                             int64_t ldc, int c_bf16, hipStream_t s) {
-    using G = LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS>;
-    const int64_t tiles = ((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN);
-    if (c_bf16) k_gemm_lds<true, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
-    else k_gemm_lds<false, G><<<(unsigned)tiles, 64 * G::NW, 0, s>>>(a, sa, b, sb, c, M, N, K, ldc, ma, mb);
-    return hipGetLastError();
+    if (K >= 512)
+        return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS, 4>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
+    return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS, 1>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
 }
 
 template <int FA>
