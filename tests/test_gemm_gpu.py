@@ -415,3 +415,44 @@ def test_full_size_sampled():
     want16 = oracle.bf16_bits_to_f32(bf16_of(want))
     assert rel_frob(got, want16) <= 1e-3
     assert np.mean(got != want16) < 0.01
+
+
+# ---- non-finite inputs: the quantizer's NaN block scale through every path ----
+NAN_CASES = [("mxfp4", "mxfp4", 1024), ("mxfp4", "mxfp4", 384), ("mxfp4", "mxfp4", 96), ("e2m3", "mxfp4", 384),
+             ("nvfp4", "nvfp4", 1024), ("nvfp4", "nvfp4", 96), ("ue5m3", "ue5m3", 1024), ("nvfp4", "mxfp4", 1024)]
+
+
+def nan_formats(kind):
+    return {"mxfp4": (mx.MXFP4, oracle.Format()),
+            "e2m3": (mx.Format(elem=mx.ELEM_FP6_E2M3), oracle.Format(elem=oracle.FP6_E2M3)),
+            "nvfp4": (mx.Format(scale=mx.SCALE_NVFP4, block_cols=16),
+                      oracle.Format(scale=oracle.SC_NVFP4, block_cols=16)),
+            "ue5m3": (mx.Format(scale=mx.SCALE_UE5M3, block_cols=16),
+                      oracle.Format(scale=oracle.SC_UE5M3, block_cols=16))}[kind]
+
+
+@pytest.mark.parametrize("ka,kb,K", NAN_CASES)
+def test_nonfinite_block_propagates(ka, kb, K):
+    """A block holding NaN or Inf gets the NaN scale code (E8M0 0xFF; UE4M3
+    0x7F; UE5M3 0xFF) and zero codes, so its dequantized values are NaN; in
+    the product that makes the block's row of A (column of B) all NaN, on the
+    native scaled instruction (the hardware's E8M0 NaN), the LDS-staged and
+    register-only kernels and both decode routes alike.  The rest of C
+    matches the oracle's product."""
+    rng = np.random.default_rng(K + len(ka))
+    M, N = 40, 48
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((N, K)).astype(np.float32)
+    a[3, 5] = np.nan
+    b[7, K - 1] = np.inf
+    (fa, ra), (fb, rb) = nan_formats(ka), nan_formats(kb)
+    qa, _, _ = mx.mx_quantize(fa, to_dev(a))
+    qb, _, _ = mx.mx_quantize(fb, to_dev(b))
+    da, db = oracle.quantize(a, ra)["dequant"], oracle.quantize(b, rb)["dequant"]
+    with np.errstate(invalid="ignore"):
+        ref = oracle.gemm_f64(da, db)
+    c = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(np.isnan(c), np.isnan(ref))
+    assert np.isnan(c[3]).all() and np.isnan(c[:, 7]).all()
+    fin = ~np.isnan(ref)
+    assert rel_frob(c[fin], ref[fin]) <= 1e-5
