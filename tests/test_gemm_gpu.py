@@ -456,3 +456,29 @@ def test_nonfinite_block_propagates(ka, kb, K):
     assert np.isnan(c[3]).all() and np.isnan(c[:, 7]).all()
     fin = ~np.isnan(ref)
     assert rel_frob(c[fin], ref[fin]) <= 1e-5
+
+
+# ---- C as a strided view: every kernel's store path ---------------------------
+@pytest.mark.parametrize("kind,K", [("mxfp4", 1024), ("mxfp4", 384), ("mxfp4", 96), ("e2m3", 384), ("nvfp4", 1024),
+                                    ("nvfp4", 96)])
+@pytest.mark.parametrize("pad", [8, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_strided_output(kind, K, pad, dtype):
+    """C written into the first N columns of a wider buffer (row stride
+    N + pad elements; pad 8 keeps bf16 rows 16-byte aligned for the tiled
+    kernel's vector stores, pad 3 does not): the same values as a dense C and
+    the padding columns untouched."""
+    rng = np.random.default_rng(K + pad)
+    M, N = 300, 264
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((N, K)).astype(np.float32)
+    (fa, _), (fb, _) = nan_formats(kind), nan_formats("mxfp4" if kind == "e2m3" else kind)
+    qa, _, _ = mx.mx_quantize(fa, to_dev(a))
+    qb, _, _ = mx.mx_quantize(fb, to_dev(b))
+    dense = mx.mx_gemm(fa, qa, fb, qb, out_dtype=dtype)
+    big = torch.full((M, N + pad), 7.0, dtype=dtype, device=dense.device)
+    view = big[:, :N]
+    mx.mx_gemm(fa, qa, fb, qb, c=view)
+    torch.cuda.synchronize()
+    assert torch.equal(view, dense)
+    assert bool((big[:, N:] == 7.0).all())
