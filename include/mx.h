@@ -196,14 +196,18 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  *    partial product is multiplied by the two rows' UE4M3 macro scales).
  *  - E2M1 elements under UE4M3, NVFP4 (UE4M3 + fp32 tensor scale), UE5M3 or
  *    E8M0 scales on 1 x b blocks, b a multiple of 8 (when the other operand
- *    is not of the kind above): each lane decodes its codes to bf16 exactly
- *    and the bf16 matrix instruction multiplies.
+ *    is not of the kind above): the codes times their block scales are
+ *    decoded exactly, to fp16 when both operands have UE4M3 scales and to
+ *    bf16 otherwise, and the fp16 / bf16 matrix instruction multiplies.
  * Anything else (INT4 / E3M0 elements, asymmetric, rotated, column or 2D
  * blocks, macro scales on FP6): MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
  * whole blocks (MX_ERR_ARG otherwise); any M, N.  E8M0 products with K a
  * multiple of 128 run on LDS-staged kernels (MXFP4 x MXFP4 without macro
- * scales and K a multiple of 1024 on the most tuned one), other K and the
- * fp8-scaled formats on register-only kernels.  macro_scales must be set when
+ * scales and K a multiple of 1024 on the most tuned one), other K on a
+ * register-only kernel; the decoded formats with 1 x 16 or 1 x 32 blocks and
+ * K a multiple of 128 on an LDS-staged kernel, the rest register-only.  A
+ * block whose scale code is NaN (E8M0 0xFF, UE4M3 0x7F, UE5M3 0xFF) makes its
+ * row of C (column, for B) NaN.  macro_scales must be set when
  * the format has macro_cols, tensor_scale for NVFP4 (MX_ERR_ARG).          */
 int mx_gemm(const mx_format *fa, const mx_qtensor *a, const mx_format *fb,
             const mx_qtensor *b, void *c, int64_t ldc, int c_dtype, void *stream);

@@ -271,9 +271,11 @@ def mx_qsnr(ref: torch.Tensor, approx: torch.Tensor, workspace=None, stream=None
 
 
 def mx_gemm(fa: Format, a: QTensor, fb: Format, b: QTensor, c=None, out_dtype=torch.bfloat16, stream=None):
-    """C = deq(A) . deq(B)^T for A (M x K) and B (N x K), each MXFP4 or MXFP6
-    (E2M3 / E3M2) with E8M0 scales per 1 x 32 block; MXFP4 operands may carry
-    1 x 128 macro-block scales (macro_cols=128)."""
+    """C = deq(A) . deq(B)^T for A (M x K) and B (N x K): MXFP4 or MXFP6 (E2M3 /
+    E3M2) with E8M0 scales per 1 x 32 block, in any pairing (MXFP4 operands may
+    carry 1 x 128 macro-block scales, macro_cols=128); or E2M1 under UE4M3,
+    NVFP4, UE5M3 or E8M0 scales on other row blocks.  c: an M x N view (any
+    row stride) to write into, else a new tensor of out_dtype."""
     if c is None:
         c = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
     ldc = c.stride(0) if a.rows > 1 else b.rows
