@@ -81,7 +81,7 @@ def gemm_formats(mx, torch, a, b, C, R, dev, reps=5):
         ("MXFP6 E2M3 x MXFP6 E2M3", fp6, fp6, "fp6 MFMA, LDS-staged 256x256 tiles", FP4_PEAK_TFLOPS),
         ("MXFP6 E3M2 x MXFP6 E3M2", fp6b, fp6b, "fp6 MFMA, LDS-staged 256x256 tiles", FP4_PEAK_TFLOPS),
         ("MXFP6 E2M3 x MXFP4", fp6, mx.MXFP4, "fp6 x fp4 MFMA, LDS-staged 256x256 tiles", FP4_PEAK_TFLOPS),
-        ("MXFP4-MBS x MXFP4-MBS", F(macro_cols=128), F(macro_cols=128), "fp4 MFMA + per-stage macro-scale fold, LDS-staged 128x128 tiles",
+        ("MXFP4-MBS x MXFP4-MBS", F(macro_cols=128), F(macro_cols=128), "fp4 MFMA + per-stage macro-scale fold, LDS-staged 256x256 tiles",
          FP4_PEAK_TFLOPS),
         ("NVFP4 x NVFP4", nv, nv, "fp16 MFMA after exact decode, LDS-staged 256x256 tiles", BF16_PEAK_TFLOPS),
         ("UE5M3/16 x UE5M3/16", F(scale=mx.SCALE_UE5M3, block_cols=16), F(scale=mx.SCALE_UE5M3, block_cols=16),

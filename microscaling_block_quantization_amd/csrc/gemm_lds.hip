@@ -24,6 +24,7 @@ using namespace mxd;
 
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -60,11 +61,11 @@ struct LGeo {
     static constexpr int SA = BM * Op<FA_>::R, SB = BN * Op<FB_>::R;
     // macro-block scales (MBS bit 0: A, bit 1: B; a stage is one 128-wide
     // macro block): each lane loads the bytes of its operand rows with the
-    // stage's E8M0 scales; A's go through LDS (BM bytes after the codes) to
-    // the lanes that hold those rows' accumulators
+    // stage's E8M0 scales; A's go through LDS, decoded to fp32 (4 BM bytes
+    // after the codes), to the lanes that hold those rows' accumulators
     static constexpr int NS = MBS ? TI + TJ : 1;       // macro scale registers per stage
     static constexpr int OFF_M = SA + SB;
-    static constexpr int STAGE = OFF_M + ((MBS & 1) ? BM : 0);
+    static constexpr int STAGE = OFF_M + ((MBS & 1) ? 4 * BM : 0);
     static constexpr int PA = SA / 1024, PB = SB / 1024;
     static constexpr int PW = (PA + PB) / NW;          // code DMA pieces per wave per stage
     // block scales travel in groups of SG stages, the 4 SG bytes of a row per
@@ -132,6 +133,48 @@ __device__ __forceinline__ void substep(v16f (&acc)[G::TI][G::TJ], const uint8_t
         for (int j = 0; j < G::TJ; j++)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], G::FA, G::FB, 2 * T,
                                                                        sc[i], 2 * T, sc[G::TI + j]);
+}
+
+// (MBS) one stage's product folded into the totals row tile by row tile: the
+// stage's two substeps go into fresh accumulators (a zero C operand), which
+// are then added to the total times s_M^A of each accumulator row and s_M^B
+// of its column; that product of two UE4M3 values is exact in fp32.  Only
+// the TJ fresh tiles of one row tile are live at a time.
+template <class G>
+__device__ __forceinline__ void mbs_stage(v16f (&acc)[G::TI][G::TJ], const uint8_t* __restrict__ st, int ra, int rb,
+                                          int half, const int (&sc)[G::TI + G::TJ], const float (&fb)[G::TJ]) {
+    v8i b0[G::TJ], b1[G::TJ];
+#pragma unroll
+    for (int j = 0; j < G::TJ; j++) {
+        b0[j] = frag<G::FB>(st + G::SA, rb + 32 * j, 0, half);
+        b1[j] = frag<G::FB>(st + G::SA, rb + 32 * j, 1, half);
+    }
+    const float* ms = reinterpret_cast<const float*>(st + G::OFF_M);
+    // accumulator register 4q + p holds row 8q + 4 half + p of the tile
+    const int r0 = ra - (ra & 31) + 4 * half;
+#pragma unroll
+    for (int i = 0; i < G::TI; i++) {
+        const v8i a0 = frag<G::FA>(st, ra + 32 * i, 0, half), a1 = frag<G::FA>(st, ra + 32 * i, 1, half);
+        v16f t[G::TJ];
+#pragma unroll
+        for (int j = 0; j < G::TJ; j++)
+            t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[j], v16f{}, G::FA, G::FB, 0, sc[i], 0,
+                                                                   sc[G::TI + j]);
+#pragma unroll
+        for (int j = 0; j < G::TJ; j++)
+            t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[j], t[j], G::FA, G::FB, 2, sc[i], 2,
+                                                                   sc[G::TI + j]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            v4f w = {1.f, 1.f, 1.f, 1.f};
+            if constexpr ((G::MBS & 1) != 0) w = *reinterpret_cast<const v4f*>(ms + r0 + 32 * i + 8 * q);
+#pragma unroll
+            for (int pp = 0; pp < 4; pp++)
+#pragma unroll
+                for (int j = 0; j < G::TJ; j++)
+                    acc[i][j][4 * q + pp] = __builtin_fmaf(t[j][4 * q + pp], w[pp] * fb[j], acc[i][j][4 * q + pp]);
+        }
+    }
 }
 
 // the operand panels of one tile: rows past M (N) read as zero through the
@@ -251,11 +294,11 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
     if (G::SG == 1 || (s & (G::SG - 1)) == 1) wait_vm<G::PW + G::GPW>();
     else wait_vm<G::PW>();
     if constexpr ((G::MBS & 1) != 0) {
-        // A's macro bytes of stage s to LDS for the accumulator rows (waves
-        // that share A rows write the same values)
-        uint8_t* ms = smem + (s % G::D) * G::STAGE + G::OFF_M;
+        // A's macro scales of stage s, decoded, to LDS for the accumulator
+        // rows (waves that share A rows write the same values)
+        float* ms = reinterpret_cast<float*>(smem + (s % G::D) * G::STAGE + G::OFF_M);
 #pragma unroll
-        for (int i = 0; i < G::TI; i++) ms[ra + 32 * i] = (uint8_t)cur[i];
+        for (int i = 0; i < G::TI; i++) ms[ra + 32 * i] = ue4m3(cur[i]);
     }
     // every wave's share of stage s has landed and every wave is done
     // reading slot (s + 2) % 3 (stage s - 1)
@@ -283,39 +326,10 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
         substep<0, G>(acc, st, ra, rb, half, sc);
         substep<1, G>(acc, st, ra, rb, half, sc);
     } else {
-        // the stage's product into fresh accumulators, then added to the total
-        // times the macro scales of the accumulator's rows (A) and column (B);
-        // their product is exact in fp32
-        v16f t[G::TI][G::TJ];
-#pragma unroll
-        for (int i = 0; i < G::TI; i++)
-#pragma unroll
-            for (int j = 0; j < G::TJ; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) t[i][j][r] = 0.f;
-        substep<0, G>(t, st, ra, rb, half, sc);
-        substep<1, G>(t, st, ra, rb, half, sc);
-        const uint8_t* ms = st + G::OFF_M;
         float fb[G::TJ];
 #pragma unroll
-        for (int j = 0; j < G::TJ; j++) fb[j] = ue4m3(cur[G::TI + j]);
-#pragma unroll
-        for (int i = 0; i < G::TI; i++) {
-            // accumulator register 4q + p holds row 8q + 4 half + p of the tile
-            const int r0 = ra - (ra & 31) + 4 * half;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                uint32_t w = 0x38383838u;                 // four codes of 1.0
-                if constexpr ((G::MBS & 1) != 0) w = *reinterpret_cast<const uint32_t*>(ms + r0 + 32 * i + 8 * q);
-#pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    const float fa = ue4m3((w >> (8 * p)) & 0xffu);
-#pragma unroll
-                    for (int j = 0; j < G::TJ; j++)
-                        acc[i][j][4 * q + p] = __builtin_fmaf(t[i][j][4 * q + p], fa * fb[j], acc[i][j][4 * q + p]);
-                }
-            }
-        }
+        for (int j = 0; j < G::TJ; j++) fb[j] = (G::MBS & 2) != 0 ? ue4m3(cur[G::TI + j]) : 1.f;
+        mbs_stage<G>(acc, st, ra, rb, half, sc, fb);
     }
 }
 
@@ -425,16 +439,15 @@ hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
                                                                            nullptr, nullptr);
 }
 
-// MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): 128 x 128
-// tiles (4 waves of 2 x 2 MFMA tiles), leaving registers for the per-stage
-// accumulators
+// MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): the same
+// 256 x 256 tiles, with the stage folded row tile by row tile (mbs_stage)
 template <int MBS>
 hipError_t launch_lds_mbs_t(const uint8_t* a, const uint8_t* sa, const uint8_t* ma, const uint8_t* b,
                             const uint8_t* sb, const uint8_t* mb, void* c, int64_t M, int64_t N, int64_t K,
                             int64_t ldc, int c_bf16, hipStream_t s) {
     if (K >= 512)
-        return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS, 4>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
-    return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 2, 2, 2, MBS, 1>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
+        return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 4, 4, 2, MBS, 4>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
+    return launch_lds_g<LGeo<MF_E2M1, MF_E2M1, 2, 4, 4, 2, MBS, 1>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, ma, mb);
 }
 
 template <int FA>
