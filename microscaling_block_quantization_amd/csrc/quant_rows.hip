@@ -393,8 +393,9 @@ namespace {
 // consecutive chunks; lane l takes chunks l, 64 + l, 128 + l, 192 + l, so each
 // of its four loads is one fully coalesced 1 KiB wave-load and a block of b
 // elements spans G = b / (elements per chunk) neighbouring lanes.  Waves walk
-// the tiles grid-stride and load the next tile before working on the current
-// one.  Every global access goes through a buffer resource that covers just the
+// the tiles grid-stride; without statistics each loads the next tile before
+// working on the current one, with statistics one tile at a time (eight waves
+// per SIMD then cover each other's loads).  Every global access goes through a buffer resource that covers just the
 // valid part of the tile: reads past the end return zero and writes past it
 // are dropped, so the loop has no per-lane bounds branches.
 // ---------------------------------------------------------------------------
