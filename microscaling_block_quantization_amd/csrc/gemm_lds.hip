@@ -135,14 +135,16 @@ __device__ __forceinline__ void substep(v16f (&acc)[G::TI][G::TJ], const uint8_t
                                                                        sc[i], 2 * T, sc[G::TI + j]);
 }
 
-// (MBS) one stage's product folded into the totals row tile by row tile: the
-// stage's two substeps go into fresh accumulators (a zero C operand), which
-// are then added to the total times s_M^A of each accumulator row and s_M^B
-// of its column; that product of two UE4M3 values is exact in fp32.  Only
-// the TJ fresh tiles of one row tile are live at a time.
+// (MBS) one stage's product folded into the totals tile by tile: the stage's
+// two substeps go into a fresh accumulator (a zero C operand), which is then
+// added to the total times s_M^A of each accumulator row and s_M^B of its
+// column; that product of two UE4M3 values is exact in fp32.  The next tile's
+// products are issued before this tile's fold, so the fold does not wait on
+// the matrix unit; two fresh tiles are live.
 template <class G>
 __device__ __forceinline__ void mbs_stage(v16f (&acc)[G::TI][G::TJ], const uint8_t* __restrict__ st, int ra, int rb,
                                           int half, const int (&sc)[G::TI + G::TJ], const float (&fb)[G::TJ]) {
+    constexpr int NTL = G::TI * G::TJ;
     v8i b0[G::TJ], b1[G::TJ];
 #pragma unroll
     for (int j = 0; j < G::TJ; j++) {
@@ -152,28 +154,35 @@ __device__ __forceinline__ void mbs_stage(v16f (&acc)[G::TI][G::TJ], const uint8
     const float* ms = reinterpret_cast<const float*>(st + G::OFF_M);
     // accumulator register 4q + p holds row 8q + 4 half + p of the tile
     const int r0 = ra - (ra & 31) + 4 * half;
+    v8i a0 = frag<G::FA>(st, ra, 0, half), a1 = frag<G::FA>(st, ra, 1, half);
+    auto product = [&](int k) -> v16f {
+        const int i = k / G::TJ, j = k % G::TJ;
+        const v16f t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[j], v16f{}, G::FA, G::FB, 0, sc[i], 0,
+                                                                       sc[G::TI + j]);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[j], t, G::FA, G::FB, 2, sc[i], 2,
+                                                               sc[G::TI + j]);
+    };
+    v16f tc = product(0);
 #pragma unroll
-    for (int i = 0; i < G::TI; i++) {
-        const v8i a0 = frag<G::FA>(st, ra + 32 * i, 0, half), a1 = frag<G::FA>(st, ra + 32 * i, 1, half);
-        v16f t[G::TJ];
-#pragma unroll
-        for (int j = 0; j < G::TJ; j++)
-            t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[j], v16f{}, G::FA, G::FB, 0, sc[i], 0,
-                                                                   sc[G::TI + j]);
-#pragma unroll
-        for (int j = 0; j < G::TJ; j++)
-            t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[j], t[j], G::FA, G::FB, 2, sc[i], 2,
-                                                                   sc[G::TI + j]);
+    for (int k = 0; k < NTL; k++) {
+        const int i = k / G::TJ, j = k % G::TJ;
+        v16f tn;
+        if (k + 1 < NTL) {
+            if ((k + 1) % G::TJ == 0) {
+                a0 = frag<G::FA>(st, ra + 32 * ((k + 1) / G::TJ), 0, half);
+                a1 = frag<G::FA>(st, ra + 32 * ((k + 1) / G::TJ), 1, half);
+            }
+            tn = product(k + 1);
+        }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             v4f w = {1.f, 1.f, 1.f, 1.f};
             if constexpr ((G::MBS & 1) != 0) w = *reinterpret_cast<const v4f*>(ms + r0 + 32 * i + 8 * q);
 #pragma unroll
             for (int pp = 0; pp < 4; pp++)
-#pragma unroll
-                for (int j = 0; j < G::TJ; j++)
-                    acc[i][j][4 * q + pp] = __builtin_fmaf(t[j][4 * q + pp], w[pp] * fb[j], acc[i][j][4 * q + pp]);
+                acc[i][j][4 * q + pp] = __builtin_fmaf(tc[4 * q + pp], w[pp] * fb[j], acc[i][j][4 * q + pp]);
         }
+        if (k + 1 < NTL) tc = tn;
     }
 }
 
@@ -328,7 +337,14 @@ __device__ __forceinline__ void lds_step(uint8_t* smem, const LPanels& P, int s,
     } else {
         float fb[G::TJ];
 #pragma unroll
-        for (int j = 0; j < G::TJ; j++) fb[j] = (G::MBS & 2) != 0 ? ue4m3(cur[G::TI + j]) : 1.f;
+        for (int j = 0; j < G::TJ; j++) {
+            fb[j] = ue4m3(cur[G::TI + j]);
+#if defined(__HIP_DEVICE_COMPILE__)
+            // without B macro scales fb is 1: kept opaque, so that the fold
+            // has the same shape (and register use) as with them
+            if constexpr ((G::MBS & 2) == 0) asm volatile("" : "+v"(fb[j]));
+#endif
+        }
         mbs_stage<G>(acc, st, ra, rb, half, sc, fb);
     }
 }
