@@ -456,7 +456,7 @@ hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
 }
 
 // MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): the same
-// 256 x 256 tiles, with the stage folded row tile by row tile (mbs_stage)
+// 256 x 256 tiles, with the stage folded tile by tile (mbs_stage)
 template <int MBS>
 hipError_t launch_lds_mbs_t(const uint8_t* a, const uint8_t* sa, const uint8_t* ma, const uint8_t* b,
                             const uint8_t* sb, const uint8_t* mb, void* c, int64_t M, int64_t N, int64_t K,
