@@ -188,3 +188,17 @@ def test_qsnr_rejects_before_launch():
     assert L.mx_qsnr(mx.DTYPE_F32, 1024, 2048, 100, None, ctypes.byref(d), None, 0, None) == mx.MX_ERR_WORKSPACE
     assert L.mx_qsnr(mx.DTYPE_F32, 1028, 2048, 100, None, ctypes.byref(d), 4096, 1 << 20, None) == mx.MX_ERR_ALIGN
     assert mx.mx_qsnr_workspace_size(100) > 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits with 2
+    before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert out["n_gpus"] == 2 and "one GPU only" in out["error"]
