@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/mx.h"
 #include "mx_kernels.hpp"
 
@@ -94,32 +96,54 @@ QParams make_params(const mx_format* f, int in_bf16, const void* x, int64_t rows
 
 bool needs_prepass(const mx_format* f) { return f->scale == MX_SCALE_NVFP4 || f->scale == MX_SCALE_E3M0; }
 
+// workgroups of the quantization kernel this call launches (its statistics
+// partials: one per workgroup)
 int64_t quant_grid(const QParams& p) {
     if (p.br > 1) return mxk::tiles_grid(p);
     if (mxk::rows_fast_ok(p)) return mxk::rows_fast_grid(p);
     return mxk::rows_grid(p);
 }
 
+// the largest grid any call with this format and shape can launch, whatever
+// the input dtype, the dequant output and the row stride: a dequant output or
+// a strided input moves MXFP4 from the fast kernel (grid capped) to the
+// general row kernel (one workgroup per 256 chunks)
+int64_t max_quant_grid(QParams p) {
+    int64_t g = 0;
+    for (int bf = 0; bf < 2; bf++) {
+        p.in_bf16 = bf;
+        if (p.br > 1) {
+            g = std::max(g, mxk::tiles_grid(p));
+            continue;
+        }
+        g = std::max(g, mxk::rows_grid(p));
+        p.dq = nullptr;
+        p.ld = p.cols;
+        if (mxk::rows_fast_ok(p)) g = std::max(g, mxk::rows_fast_grid(p));
+    }
+    return g;
+}
+
 struct Workspace {
     size_t stats_off, stats_bytes, amax_off, amax_bytes, total;
 };
 
-Workspace workspace_layout(const mx_format* f, int in_bf16, int64_t rows, int64_t cols) {
+// One layout per format and shape, valid for both input dtypes and every
+// kernel route, so that mx_query_sizes needs neither.
+Workspace workspace_layout(const mx_format* f, int64_t rows, int64_t cols) {
     mx_qtensor dummy;
     memset(&dummy, 0, sizeof(dummy));
-    QParams p = make_params(f, in_bf16, nullptr, rows, cols, cols, &dummy);
+    QParams p = make_params(f, 1, nullptr, rows, cols, cols, &dummy);
     Workspace w;
-    // sized for the larger of the two input dtypes' grids so one query fits both
-    p.in_bf16 = 0;
-    int64_t g0 = quant_grid(p);
-    p.in_bf16 = 1;
-    int64_t g1 = quant_grid(p);
-    int64_t g = g0 > g1 ? g0 : g1;
-    (void)in_bf16;
     w.stats_off = 0;
-    w.stats_bytes = round_up((size_t)g * sizeof(mxd::StatPart));
+    w.stats_bytes = round_up((size_t)max_quant_grid(p) * sizeof(mxd::StatPart));
     w.amax_off = w.stats_off + w.stats_bytes;
-    w.amax_bytes = needs_prepass(f) ? round_up((size_t)mxk::amax_grid(p) * sizeof(float)) : 0;
+    int64_t ga = 0;
+    for (int bf = 0; bf < 2; bf++) {
+        p.in_bf16 = bf;
+        ga = std::max(ga, mxk::amax_grid(p));
+    }
+    w.amax_bytes = needs_prepass(f) ? round_up((size_t)ga * sizeof(float)) : 0;
     w.total = w.amax_off + w.amax_bytes;
     return w;
 }
@@ -153,7 +177,7 @@ int mx_query_sizes(const mx_format* f, int64_t rows, int64_t cols, mx_sizes* out
     out->macro_scales = f->macro_cols ? (size_t)(rows * (cols / 128)) : 0;
     out->tensor_scale = f->scale == MX_SCALE_NVFP4 ? sizeof(float) : 0;
     out->ref_exp = f->scale == MX_SCALE_E3M0 ? sizeof(int32_t) : 0;
-    out->workspace = workspace_layout(f, 1, rows, cols).total;
+    out->workspace = workspace_layout(f, rows, cols).total;
     return MX_OK;
 }
 
@@ -174,7 +198,7 @@ int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, i
     const int esz = in_dtype == MX_DTYPE_BF16 ? 2 : 4;
     if (!aligned16(x) || !aligned16(out->codes) || !aligned16(dequant) || ((ld * esz) & 15)) return MX_ERR_ALIGN;
     if (!aligned16(out->offsets) || !aligned16(stats)) return MX_ERR_ALIGN;
-    const Workspace W = workspace_layout(f, in_dtype == MX_DTYPE_BF16, rows, cols);
+    const Workspace W = workspace_layout(f, rows, cols);
     const bool need_ws = stats || needs_prepass(f);
     if (need_ws && (!workspace || ws_bytes < W.total)) return MX_ERR_WORKSPACE;
     if (need_ws && !aligned16(workspace)) return MX_ERR_ALIGN;
@@ -199,7 +223,11 @@ int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, i
         if (rc) return rc;
     }
     int64_t grid = n > 0 ? quant_grid(p) : 0;
-    if (stats) p.parts = reinterpret_cast<mxd::StatPart*>(ws + W.stats_off);
+    if (stats) {
+        // the layout covers every route; this guards the route taken
+        if ((size_t)grid * sizeof(mxd::StatPart) > W.stats_bytes) return MX_ERR_WORKSPACE;
+        p.parts = reinterpret_cast<mxd::StatPart*>(ws + W.stats_off);
+    }
     if (grid > 0) {
         hipError_t e;
         if (p.br > 1) e = mxk::launch_tiles(p, s);

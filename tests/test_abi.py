@@ -74,6 +74,41 @@ def test_query_sizes_mxfp4_and_nvfp4():
     assert s["ref_exp"] == 4
 
 
+STAT_PART_BYTES = 48          # one statistics partial per workgroup of the quantizer
+
+
+def _rows_grid(rows, cols):
+    """workgroups of the general row kernel: 256 threads of 16 (8 when cols is
+    8 mod 16) consecutive elements each"""
+    ch = 16 if cols % 16 == 0 else 8
+    return -(-rows * (cols // ch) // 256)
+
+
+def _tiles_grid(rows, cols, br, in_bf16):
+    return -(-(rows // br) * (cols // (8 if in_bf16 else 4)) // 256)
+
+
+@pytest.mark.parametrize("rows,cols,kw", [
+    (8192, 4096, {}), (4096, 14336, {}), (14336, 4096, {}), (256, 1032, dict(block_cols=8)),
+    (1024, 1024, dict(block_cols=16)), (8192, 4096, dict(scale=mx.SCALE_NVFP4, block_cols=16)),
+    (96, 512, dict(block_rows=32, block_cols=1)), (4096, 14336, dict(block_rows=32, block_cols=32)),
+    (4096, 14336, dict(block_rows=8, block_cols=8)),
+])
+def test_workspace_covers_every_kernel_route(rows, cols, kw):
+    """The statistics partials of whichever kernel a call takes fit in the
+    queried workspace: a dequant output or a strided input sends MXFP4 to the
+    general row kernel, whose grid is not capped like the fast kernel's."""
+    s = mx.mx_query_sizes(mx.Format(**kw), rows, cols)
+    br = kw.get("block_rows", 1)
+    if br == 1:
+        need = _rows_grid(rows, cols) * STAT_PART_BYTES
+    else:
+        need = max(_tiles_grid(rows, cols, br, b) for b in (0, 1)) * STAT_PART_BYTES
+    if kw.get("scale") == mx.SCALE_NVFP4:
+        need += _rows_grid(rows, cols) * 4       # the tensor pre-pass maxima
+    assert s["workspace"] >= need
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(elem=7), mx.MX_ERR_ARG),
     (dict(block_cols=24), mx.MX_ERR_ARG),
