@@ -224,6 +224,8 @@ int ref_e8m0_exponent(int rule, float tau, int elem, int asym, float amax) {
     const grid_t *G = grid_for(elem, asym);
     int e;
     if (!(amax > 0)) return -127;
+    /* a range that overflowed (max - offset beyond FLT_MAX): the largest scale */
+    if (!is_finite_f(amax)) return 127;
     if (rule == REF_RULE_FLOOR) e = flog2(amax) - G->emax;
     else if (rule == REF_RULE_CEIL) e = e_ceil(amax, G->qmax);
     else e = e_ceil(amax, (double)tau);
@@ -452,8 +454,10 @@ static void quantize_block(const qctx *q, int64_t bi, int64_t bj) {
     }
 
     if (f->asymmetric) {
-        /* E2M1 with a bf16 mid-range offset, then symmetric scaling of the rest */
-        uint16_t ob = bf16_nearest((mx + mn) * 0.5f);
+        /* E2M1 with a bf16 mid-range offset, then symmetric scaling of the rest.
+         * The mid-range halves each end before adding (exact for normal values),
+         * so it cannot overflow when both ends are near FLT_MAX. */
+        uint16_t ob = bf16_nearest(mx * 0.5f + mn * 0.5f);
         float o = bf16_to_float(ob);
         float ymax = 0;
         int e;
