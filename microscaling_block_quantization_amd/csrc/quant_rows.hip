@@ -262,7 +262,8 @@ __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
                 float R = mx - o;
                 e = R > 0.f ? e8m0_exp(p.rule, p.tau, E, R) : -127;
             } else {
-                ob = bf16_rne((mx + mn) * 0.5f);
+                // the mid-range, each end halved first so that it cannot overflow
+                ob = bf16_rne(mx * 0.5f + mn * 0.5f);
                 o = bf16f(ob);
                 float ym = 0.f;
 #pragma unroll

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                 float R = mx[j] - o[j];
                 e[j] = R > 0.f ? e8m0_exp(p.rule, p.tau, E, R) : -127;
             } else {
-                ob[j] = bf16_rne((mx[j] + mn[j]) * 0.5f);
+                // the mid-range, each end halved first so that it cannot overflow
+                ob[j] = bf16_rne(mx[j] * 0.5f + mn[j] * 0.5f);
                 o[j] = bf16f(ob[j]);
             }
         } else if (p.scale == SC_E8M0) {

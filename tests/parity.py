@@ -23,11 +23,15 @@ def host_u8(t, n):
     return t.detach().cpu().numpy().reshape(-1)[:n]
 
 
-def run_gpu(x, kw, dq_dtype=torch.float32):
+def run_gpu(x, kw, dq_dtype=torch.float32, stats=True):
+    """One mx_quantize call.  dq_dtype None asks for no dequantized output:
+    MXFP4 (E2M1, E8M0 scales, RTNE, dense rows) then takes the fast kernel,
+    which is the one the benchmark times; any other output set takes the
+    general kernels."""
     xd = to_dev(x)
-    q, dq, st = mx.mx_quantize(mx.Format(**kw), xd, dequant=dq_dtype, stats=True)
+    q, dq, st = mx.mx_quantize(mx.Format(**kw), xd, dequant=dq_dtype, stats=True if stats else None)
     torch.cuda.synchronize()
-    return q, dq, mx.stats_to_dict(st)
+    return q, dq, (mx.stats_to_dict(st) if stats else None)
 
 
 def bits_equal_f32(a, b):
@@ -45,15 +49,12 @@ def qsnr_of(st):
     return 10 * math.log10(st["sig2"] / st["err2"])
 
 
-def check_quantize(x, kw, label="", dq_dtype=torch.float32):
-    """Full element-by-element parity of one quantization call."""
-    ref = oracle.quantize(x, oracle.Format(**kw),
-                          dq_dtype=oracle.BF16 if dq_dtype == torch.bfloat16 else oracle.F32)
-    q, dq, st = run_gpu(x, kw, dq_dtype)
-    rows, cols = x.shape
+def compare_codes(ref, q, label):
+    """codes, scales and the format's side outputs, bit for bit"""
     codes = host_u8(q.codes, ref["codes"].size).reshape(ref["codes"].shape)
     bad = np.argwhere(codes != ref["codes"])
-    assert bad.size == 0, f"{label}: {len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+    assert bad.size == 0, f"{label}: {len(bad)} code bytes differ, first at {bad[:3].tolist()}: " \
+        f"gpu {codes[tuple(bad[0])]:#04x} ref {ref['codes'][tuple(bad[0])]:#04x}"
     scales = host_u8(q.scales, ref["scales"].size).reshape(ref["scales"].shape)
     bad = np.argwhere(scales != ref["scales"])
     assert bad.size == 0, f"{label}: {len(bad)} scales differ, first at {bad[:3].tolist()}: " \
@@ -68,14 +69,10 @@ def check_quantize(x, kw, label="", dq_dtype=torch.float32):
         assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == ref["tensor_scale"].view(np.uint32)[0], label
     if ref["ref_exp"] is not None:
         assert int(q.ref_exp.cpu()[0]) == int(ref["ref_exp"][0]), label
-    if dq_dtype == torch.bfloat16:
-        got = dq.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert np.array_equal(got, ref["dequant"]), f"{label}: bf16 dequant differs"
-    else:
-        got = dq.cpu().numpy()
-        assert bits_equal_f32(got, ref["dequant"]), f"{label}: dequant differs at " \
-            f"{np.argwhere(got.view(np.uint32) != ref['dequant'].view(np.uint32))[:3].tolist()}"
-    rs = ref["stats"]
+
+
+def compare_stats(rs, st, label):
+    """counts exactly, QSNR within the contract's tolerance"""
     for k in ("n", "nonzero", "flushed", "zero_blocks"):
         assert st[k] == rs[k], f"{label}: stats {k} {st[k]} != {rs[k]}"
     if math.isfinite(rs["sig2"]) and rs["sig2"] > 0:
@@ -83,7 +80,33 @@ def check_quantize(x, kw, label="", dq_dtype=torch.float32):
         if math.isfinite(b):
             assert abs(a - b) <= QSNR_TOL_DB, f"{label}: QSNR {a} vs {b}"
         else:
-            assert a == b
+            assert a == b, f"{label}: QSNR {a} vs {b}"
+
+
+def check_quantize(x, kw, label="", dq_dtype=torch.float32):
+    """Full element-by-element parity of one quantization, through every
+    output set a caller can ask for: with a dequantized output and statistics
+    (the general kernels), with statistics only, and codes only (for MXFP4
+    these two take the fast kernel).  Each route is held to the oracle:
+    codes, scales and side outputs bit for bit, dequantized values bit for
+    bit, counts exactly, QSNR within 1e-4 dB."""
+    ref = oracle.quantize(x, oracle.Format(**kw),
+                          dq_dtype=oracle.BF16 if dq_dtype == torch.bfloat16 else oracle.F32)
+    q, dq, st = run_gpu(x, kw, dq_dtype)
+    compare_codes(ref, q, f"{label} [dequant+stats]")
+    if dq_dtype == torch.bfloat16:
+        got = dq.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref["dequant"]), f"{label}: bf16 dequant differs"
+    else:
+        got = dq.cpu().numpy()
+        assert bits_equal_f32(got, ref["dequant"]), f"{label}: dequant differs at " \
+            f"{np.argwhere(got.view(np.uint32) != ref['dequant'].view(np.uint32))[:3].tolist()}"
+    compare_stats(ref["stats"], st, f"{label} [dequant+stats]")
+    q2, _, st2 = run_gpu(x, kw, None, stats=True)
+    compare_codes(ref, q2, f"{label} [stats]")
+    compare_stats(ref["stats"], st2, f"{label} [stats]")
+    q3, _, _ = run_gpu(x, kw, None, stats=False)
+    compare_codes(ref, q3, f"{label} [codes]")
     return ref, q
 
 
