@@ -30,7 +30,9 @@
  *  - Every tensor pointer is a DEVICE pointer (memory of the current HIP
  *    device) unless the argument says "host".  The caller allocates and owns
  *    every buffer; the library allocates nothing and keeps no state between
- *    calls, so calls from several host threads on different streams are safe.
+ *    calls, so calls from several host threads on different streams are safe
+ *    (the one exception, mx_quantize_noalloc, keeps a static scratch array
+ *    per GPU; see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued and the call returns at once, except mx_qsnr, which waits.
  *  - Return value: MX_OK, or an MX_ERR_* code.  Every argument is checked
@@ -55,6 +57,8 @@ extern "C" {
 #define MX_ERR_ALIGN 3        /* pointer or leading dimension not aligned    */
 #define MX_ERR_WORKSPACE 4    /* workspace missing or smaller than required  */
 #define MX_ERR_HIP 5          /* a HIP launch failed                         */
+#define MX_ERR_TOO_LARGE 6    /* mx_quantize_noalloc: the call needs more    *
+                               * scratch than its static array holds         */
 
 /* ---- element types [A], [U] --------------------------------------------
  * Codes are sign-magnitude unless noted; no format has Inf or NaN and every
@@ -168,6 +172,29 @@ int mx_quantize(const mx_format *f, int in_dtype, const void *x, int64_t rows,
                 int64_t cols, int64_t ld, const mx_qtensor *out, void *dequant,
                 int dq_dtype, mx_stats *stats, void *workspace, size_t ws_bytes,
                 void *stream);
+
+/* mx_quantize without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It runs the same kernels as mx_quantize;
+ * what they need beyond the caller's inputs and outputs (the statistics
+ * partials and the NVFP4 / E3M0 pre-pass maxima) goes into a static device
+ * array of MX_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends.  The call itself allocates nothing (no hipMalloc,
+ * no allocating library routine).  Its first call on a device looks up that
+ * device's address of the array.
+ *  - Limit: a call whose mx_query_sizes().workspace exceeds
+ *    MX_NOALLOC_SCRATCH_BYTES returns MX_ERR_TOO_LARGE before any launch
+ *    (4 MiB holds the statistics of about 350 M elements of row blocks).
+ *    Calls that need no workspace (no statistics, no pre-pass) have no limit.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in
+ *    time on one GPU (two streams, two host threads) race and give wrong
+ *    statistics or tensor scales.  Serialise them.  No initial contents are
+ *    needed: every call writes what it reads.
+ * Other arguments, errors and outputs: as mx_quantize.                      */
+#define MX_NOALLOC_SCRATCH_BYTES (4u << 20)
+int mx_quantize_noalloc(const mx_format *f, int in_dtype, const void *x, int64_t rows,
+                        int64_t cols, int64_t ld, const mx_qtensor *out, void *dequant,
+                        int dq_dtype, mx_stats *stats, void *stream);
 
 /* Dequantize q into y (rows x cols, row stride ld elements, dtype out_dtype). */
 int mx_dequantize(const mx_format *f, const mx_qtensor *q, int out_dtype, void *y,

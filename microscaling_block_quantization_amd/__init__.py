@@ -25,15 +25,16 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmx.so")
 
-MX_OK, MX_ERR_ARG, MX_ERR_UNSUPPORTED, MX_ERR_ALIGN, MX_ERR_WORKSPACE, MX_ERR_HIP = range(6)
+MX_OK, MX_ERR_ARG, MX_ERR_UNSUPPORTED, MX_ERR_ALIGN, MX_ERR_WORKSPACE, MX_ERR_HIP, MX_ERR_TOO_LARGE = range(7)
+NOALLOC_SCRATCH_BYTES = 4 << 20      # MX_NOALLOC_SCRATCH_BYTES of include/mx.h
 ELEM_E2M1, ELEM_INT4, ELEM_FP6_E2M3, ELEM_FP6_E3M2, ELEM_E3M0 = range(5)
 SCALE_E8M0, SCALE_UE4M3, SCALE_NVFP4, SCALE_UE5M3, SCALE_E3M0 = range(5)
 RULE_FLOOR, RULE_CEIL, RULE_OAS = range(3)
 ROUND_RTNE, ROUND_SR, ROUND_CEIL = range(3)
 DTYPE_F32, DTYPE_BF16 = range(2)
 
-EXPORTS = ["mx_query_sizes", "mx_quantize", "mx_dequantize", "mx_qsnr_workspace_size",
-           "mx_qsnr", "mx_gemm", "mx_status_string"]
+EXPORTS = ["mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_dequantize",
+           "mx_qsnr_workspace_size", "mx_qsnr", "mx_gemm", "mx_status_string"]
 
 
 class MxFormat(ctypes.Structure):
@@ -87,6 +88,7 @@ def lib():
         L.mx_query_sizes.argtypes = [P(MxFormat), i64, i64, P(MxSizes)]
         L.mx_quantize.argtypes = [P(MxFormat), i32, vp, i64, i64, i64, P(MxQTensor), vp, i32, vp,
                                   vp, ctypes.c_size_t, vp]
+        L.mx_quantize_noalloc.argtypes = [P(MxFormat), i32, vp, i64, i64, i64, P(MxQTensor), vp, i32, vp, vp]
         L.mx_dequantize.argtypes = [P(MxFormat), P(MxQTensor), i32, vp, i64, vp]
         L.mx_qsnr_workspace_size.argtypes = [i64]
         L.mx_qsnr_workspace_size.restype = ctypes.c_size_t
@@ -95,7 +97,8 @@ def lib():
         L.mx_gemm.argtypes = [P(MxFormat), P(MxQTensor), P(MxFormat), P(MxQTensor), vp, i64, i32, vp]
         L.mx_status_string.argtypes = [i32]
         L.mx_status_string.restype = ctypes.c_char_p
-        for name in ("mx_query_sizes", "mx_quantize", "mx_dequantize", "mx_qsnr", "mx_gemm"):
+        for name in ("mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_dequantize", "mx_qsnr",
+                     "mx_gemm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,6 +240,25 @@ def mx_quantize(fmt: Format, x: torch.Tensor, out: QTensor = None, dequant=None,
                            _ptr(stats), _ptr(workspace),
                            0 if workspace is None else workspace.numel(), _stream(stream))
     _check(rc, "mx_quantize")
+    return out, dequant, stats
+
+
+def mx_quantize_noalloc(fmt: Format, x: torch.Tensor, out: QTensor, dequant=None, stats=None, stream=None):
+    """mx_quantize without a workspace: the library's static scratch array on
+    this GPU holds what its kernels need beyond the outputs (at most
+    NOALLOC_SCRATCH_BYTES; larger calls raise MxError MX_ERR_TOO_LARGE).  The
+    outputs are the caller's: `out` (a QTensor), `dequant` (None or a tensor)
+    and `stats` (None or a 48-byte device tensor).  Calls that overlap on one
+    GPU share the array and race."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else cols
+    f = fmt.c()
+    q = out.c()
+    rc = lib().mx_quantize_noalloc(ctypes.byref(f), _dtype_code(x), _ptr(x), rows, cols, ld, ctypes.byref(q),
+                                   _ptr(dequant), DTYPE_F32 if dequant is None else _dtype_code(dequant),
+                                   _ptr(stats), _stream(stream))
+    _check(rc, "mx_quantize_noalloc")
     return out, dequant, stats
 
 

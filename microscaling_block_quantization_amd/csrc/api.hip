@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/mx.h"
 #include "mx_kernels.hpp"
@@ -150,40 +151,9 @@ Workspace workspace_layout(const mx_format* f, int64_t rows, int64_t cols) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-const char* mx_status_string(int status) {
-    switch (status) {
-    case MX_OK: return "ok";
-    case MX_ERR_ARG: return "invalid argument";
-    case MX_ERR_UNSUPPORTED: return "format or shape not supported by this build";
-    case MX_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
-    case MX_ERR_WORKSPACE: return "workspace missing or too small";
-    case MX_ERR_HIP: return "HIP launch failed";
-    default: return "unknown status";
-    }
-}
-
-int mx_query_sizes(const mx_format* f, int64_t rows, int64_t cols, mx_sizes* out) {
-    int rc = check_format(f, rows, cols);
-    if (rc) return rc;
-    if (!out) return MX_ERR_ARG;
-    const int64_t nblk = (rows / f->block_rows) * (cols / f->block_cols);
-    out->codes = (size_t)(rows * crow_bytes(f, cols));
-    out->scales = (size_t)nblk;
-    out->offsets = f->asymmetric ? (size_t)nblk * 2 : 0;
-    out->macro_scales = f->macro_cols ? (size_t)(rows * (cols / 128)) : 0;
-    out->tensor_scale = f->scale == MX_SCALE_NVFP4 ? sizeof(float) : 0;
-    out->ref_exp = f->scale == MX_SCALE_E3M0 ? sizeof(int32_t) : 0;
-    out->workspace = workspace_layout(f, rows, cols).total;
-    return MX_OK;
-}
-
-int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
-                const mx_qtensor* out, void* dequant, int dq_dtype, mx_stats* stats, void* workspace,
-                size_t ws_bytes, void* stream) {
+// Every check of mx_quantize except the workspace's.
+int check_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                   const mx_qtensor* out, const void* dequant, int dq_dtype, const mx_stats* stats) {
     int rc = check_format(f, rows, cols);
     if (rc) return rc;
     if (in_dtype != MX_DTYPE_F32 && in_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
@@ -198,16 +168,19 @@ int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, i
     const int esz = in_dtype == MX_DTYPE_BF16 ? 2 : 4;
     if (!aligned16(x) || !aligned16(out->codes) || !aligned16(dequant) || ((ld * esz) & 15)) return MX_ERR_ALIGN;
     if (!aligned16(out->offsets) || !aligned16(stats)) return MX_ERR_ALIGN;
-    const Workspace W = workspace_layout(f, rows, cols);
-    const bool need_ws = stats || needs_prepass(f);
-    if (need_ws && (!workspace || ws_bytes < W.total)) return MX_ERR_WORKSPACE;
-    if (need_ws && !aligned16(workspace)) return MX_ERR_ALIGN;
+    return MX_OK;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// The launches of one quantization, its arguments already checked.  ws: the
+// workspace laid out as W (unused, and may be null, when the call needs none).
+int launch_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                    const mx_qtensor* out, void* dequant, int dq_dtype, mx_stats* stats, uint8_t* ws,
+                    const Workspace& W, hipStream_t s) {
+    int rc;
+    const int64_t n = rows * cols;
     QParams p = make_params(f, in_dtype == MX_DTYPE_BF16, x, rows, cols, ld, out);
     p.dq = dequant;
     p.dq_bf16 = dq_dtype == MX_DTYPE_BF16;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
 
     if (needs_prepass(f)) {
         QParams a = p;
@@ -241,6 +214,92 @@ int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, i
         if (rc) return rc;
     }
     return MX_OK;
+}
+
+// ---- the static scratch of mx_quantize_noalloc -----------------------------
+// One copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only names the symbol): it takes
+// the device address hipGetSymbolAddress gives on each device, once per
+// device, and passes that.
+__device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<uint8_t*> scratch_ptr[MAX_DEVICES];
+
+// The current device's address of `scratch`.
+int static_scratch(uint8_t** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MX_ERR_HIP;
+    uint8_t* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return MX_ERR_HIP;
+        p = static_cast<uint8_t*>(a);
+        scratch_ptr[dev].store(p, std::memory_order_release);   // the same address if two threads race here
+    }
+    *ptr = p;
+    return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(int status) {
+    switch (status) {
+    case MX_OK: return "ok";
+    case MX_ERR_ARG: return "invalid argument";
+    case MX_ERR_UNSUPPORTED: return "format or shape not supported by this build";
+    case MX_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case MX_ERR_WORKSPACE: return "workspace missing or too small";
+    case MX_ERR_HIP: return "HIP launch failed";
+    case MX_ERR_TOO_LARGE: return "tensor needs more scratch than mx_quantize_noalloc's static array holds";
+    default: return "unknown status";
+    }
+}
+
+int mx_query_sizes(const mx_format* f, int64_t rows, int64_t cols, mx_sizes* out) {
+    int rc = check_format(f, rows, cols);
+    if (rc) return rc;
+    if (!out) return MX_ERR_ARG;
+    const int64_t nblk = (rows / f->block_rows) * (cols / f->block_cols);
+    out->codes = (size_t)(rows * crow_bytes(f, cols));
+    out->scales = (size_t)nblk;
+    out->offsets = f->asymmetric ? (size_t)nblk * 2 : 0;
+    out->macro_scales = f->macro_cols ? (size_t)(rows * (cols / 128)) : 0;
+    out->tensor_scale = f->scale == MX_SCALE_NVFP4 ? sizeof(float) : 0;
+    out->ref_exp = f->scale == MX_SCALE_E3M0 ? sizeof(int32_t) : 0;
+    out->workspace = workspace_layout(f, rows, cols).total;
+    return MX_OK;
+}
+
+int mx_quantize(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                const mx_qtensor* out, void* dequant, int dq_dtype, mx_stats* stats, void* workspace,
+                size_t ws_bytes, void* stream) {
+    int rc = check_quantize(f, in_dtype, x, rows, cols, ld, out, dequant, dq_dtype, stats);
+    if (rc) return rc;
+    const Workspace W = workspace_layout(f, rows, cols);
+    const bool need_ws = stats || needs_prepass(f);
+    if (need_ws && (!workspace || ws_bytes < W.total)) return MX_ERR_WORKSPACE;
+    if (need_ws && !aligned16(workspace)) return MX_ERR_ALIGN;
+    return launch_quantize(f, in_dtype, x, rows, cols, ld, out, dequant, dq_dtype, stats,
+                           static_cast<uint8_t*>(workspace), W, static_cast<hipStream_t>(stream));
+}
+
+int mx_quantize_noalloc(const mx_format* f, int in_dtype, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                        const mx_qtensor* out, void* dequant, int dq_dtype, mx_stats* stats, void* stream) {
+    int rc = check_quantize(f, in_dtype, x, rows, cols, ld, out, dequant, dq_dtype, stats);
+    if (rc) return rc;
+    const Workspace W = workspace_layout(f, rows, cols);
+    const bool need_ws = stats || needs_prepass(f);
+    if (need_ws && W.total > MX_NOALLOC_SCRATCH_BYTES) return MX_ERR_TOO_LARGE;
+    uint8_t* ws = nullptr;
+    if (need_ws) {
+        rc = static_scratch(&ws);
+        if (rc) return rc;
+    }
+    return launch_quantize(f, in_dtype, x, rows, cols, ld, out, dequant, dq_dtype, stats, ws, W,
+                           static_cast<hipStream_t>(stream));
 }
 
 int mx_dequantize(const mx_format* f, const mx_qtensor* q, int out_dtype, void* y, int64_t ld, void* stream) {

@@ -45,7 +45,7 @@ def test_struct_layouts_match_header():
 
 def test_status_strings():
     assert mx.mx_status_string(mx.MX_OK) == "ok"
-    for s in range(1, 6):
+    for s in range(1, 7):
         assert mx.mx_status_string(s) != "unknown status"
     assert mx.mx_status_string(99) == "unknown status"
 
@@ -237,3 +237,28 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     out = json.loads(r.stdout.strip().splitlines()[-1])
     assert out["n_gpus"] == 2 and "one GPU only" in out["error"]
+
+
+def test_noalloc_rejects_before_launch():
+    """The no-allocation entry point checks its arguments like mx_quantize, and
+    refuses (before any HIP call) a tensor whose workspace would not fit its
+    static scratch array; a call that needs no workspace has no size limit."""
+    L = mx.lib()
+
+    def call(fmt, rows, cols, stats=None, x=1024):
+        q = mx.MxQTensor(2048, 4096, None, None, 8192, None, rows, cols)
+        f = fmt.c()
+        return L.mx_quantize_noalloc(ctypes.byref(f), mx.DTYPE_BF16, x, rows, cols, cols, ctypes.byref(q), None,
+                                     mx.DTYPE_F32, stats, None)
+
+    assert call(mx.Format(), 4, 64, x=None) == mx.MX_ERR_ARG
+    assert call(mx.Format(), 4, 64, x=1032) == mx.MX_ERR_ALIGN
+    assert call(mx.Format(block_cols=24), 4, 96) == mx.MX_ERR_ARG
+    big = (1 << 15, 1 << 15)                       # 2^30 elements: workspace far above 4 MiB
+    assert mx.mx_query_sizes(mx.MXFP4, *big)["workspace"] > mx.NOALLOC_SCRATCH_BYTES
+    assert call(mx.MXFP4, *big, stats=4096) == mx.MX_ERR_TOO_LARGE
+    assert call(mx.Format(scale=mx.SCALE_NVFP4, block_cols=16), *big) == mx.MX_ERR_TOO_LARGE
+    # the largest configured tensors fit
+    for rows, cols, kw in ((16384, 4096, {}), (4096, 14336, dict(block_rows=8, block_cols=8)),
+                           (16384, 4096, dict(scale=mx.SCALE_NVFP4, block_cols=16))):
+        assert mx.mx_query_sizes(mx.Format(**kw), rows, cols)["workspace"] <= mx.NOALLOC_SCRATCH_BYTES
