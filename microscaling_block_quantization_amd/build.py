@@ -14,6 +14,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmx.so")
+# the measurement's context kernels (copy, stream, matrix-instruction loop):
+# a library of their own, so that libmx.so exports only the method's ABI
+CEIL_LIB = os.path.join(HERE, "libmx_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "quant_rows.hip", "quant_tiles.hip", "misc.hip", "gemm_mxfp4.hip", "gemm_lds.hip", "gemm_upcvt.hip"]
 
@@ -39,17 +43,23 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB, verbose)
     return LIB
 
 

@@ -262,3 +262,20 @@ def test_noalloc_rejects_before_launch():
     for rows, cols, kw in ((16384, 4096, {}), (4096, 14336, dict(block_rows=8, block_cols=8)),
                            (16384, 4096, dict(scale=mx.SCALE_NVFP4, block_cols=16))):
         assert mx.mx_query_sizes(mx.Format(**kw), rows, cols)["workspace"] <= mx.NOALLOC_SCRATCH_BYTES
+
+
+def test_ceilings_library_exports_its_header():
+    """libmx_ceilings.so (the measurement's context kernels) exports what
+    include/mx_ceilings.h declares, and libmx.so exports none of it."""
+    from microscaling_block_quantization_amd import ceilings
+    src = open(os.path.join(ROOT, "include", "mx_ceilings.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mxc_[a-z0-9_]+)\s*\(", src)))
+    assert names == sorted(ceilings.EXPORTS)
+    nm = os.popen(f"nm -D --defined-only {ceilings.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", nm), n
+    assert "mxc_" not in os.popen(f"nm -D --defined-only {mx.LIB_PATH}").read()
+    L = ceilings.lib()
+    assert L.mxc_mfma_loop_flops(256, 10) == 2.0 * 32 * 32 * 64 * 16 * 8 * 256 * 10
+    assert L.mxc_copy(None, None, 16, None) == 1 and L.mxc_mfma_loop(None, None, 1, 1, None) == 1
