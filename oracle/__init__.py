@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmxref.so")
 
 # element types, scale types, exponent rules, rounding modes, dtypes
-E2M1, INT4, FP6_E2M3, FP6_E3M2, E3M0 = 0, 1, 2, 3, 4
+E2M1, INT4, FP6_E2M3, FP6_E3M2, E3M0, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4, 5, 6
 SC_E8M0, SC_UE4M3, SC_NVFP4, SC_UE5M3, SC_E3M0 = 0, 1, 2, 3, 4
 RULE_FLOOR, RULE_CEIL, RULE_OAS = 0, 1, 2
 RTNE, SR, CEIL = 0, 1, 2
@@ -117,11 +117,13 @@ def _ptr(a):
 
 
 def elem_bits(elem):
+    if elem in (FP8_E4M3, FP8_E5M2):
+        return 8
     return 6 if elem in (FP6_E2M3, FP6_E3M2) else 4
 
 
 def code_row_bytes(elem, cols):
-    return cols * 3 // 4 if elem_bits(elem) == 6 else cols // 2
+    return {8: cols, 6: cols * 3 // 4}.get(elem_bits(elem), cols // 2)
 
 
 def set_threads(n):

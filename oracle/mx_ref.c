@@ -79,9 +79,9 @@ static float times_pow2(float v, int k) { return (float)((double)v * ldexp(1.0, 
 /* ------------------------------------------------------------------------ */
 /* element grids (non-negative magnitudes, ascending by code index)          */
 /* ------------------------------------------------------------------------ */
-typedef struct { int n; double g[32]; double qmax; int emax; int bits; } grid_t;
+typedef struct { int n; double g[128]; double qmax; int emax; int bits; } grid_t;
 
-static grid_t G_E2M1, G_E3M0, G_INT4, G_UINT4, G_E2M3, G_E3M2;
+static grid_t G_E2M1, G_E3M0, G_INT4, G_UINT4, G_E2M3, G_E3M2, G_E4M3, G_E5M2;
 static int grids_ready = 0;
 
 static void build_grids(void) {
@@ -110,6 +110,22 @@ static void build_grids(void) {
     }
     G_E2M3.qmax = G_E2M3.g[31];
     G_E3M2.qmax = G_E3M2.g[31];
+    /* FP8 E4M3 (bias 7; magnitude code 0x7F is NaN, so the largest value is
+     * 0x7E = 448) and E5M2 (bias 15; 0x7C is Inf and above are NaN, so the
+     * largest value is 0x7B = 57344), the OCP 8-bit MX element types.  As MX
+     * elements they saturate at their largest finite value. */
+    G_E4M3.n = 127; G_E4M3.emax = 8; G_E4M3.bits = 8;
+    for (i = 0; i < 127; i++) {
+        int e = i >> 3, m = i & 7;
+        G_E4M3.g[i] = e == 0 ? m / 8.0 * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    }
+    G_E5M2.n = 124; G_E5M2.emax = 15; G_E5M2.bits = 8;
+    for (i = 0; i < 124; i++) {
+        int e = i >> 2, m = i & 3;
+        G_E5M2.g[i] = e == 0 ? m / 4.0 * ldexp(1.0, -14) : (1.0 + m / 4.0) * ldexp(1.0, e - 15);
+    }
+    G_E4M3.qmax = G_E4M3.g[126];
+    G_E5M2.qmax = G_E5M2.g[123];
     grids_ready = 1;
 }
 
@@ -121,6 +137,8 @@ static const grid_t *grid_for(int elem, int asym) {
     case REF_FP6_E2M3: return &G_E2M3;
     case REF_FP6_E3M2: return &G_E3M2;
     case REF_E3M0: return &G_E3M0;
+    case REF_FP8_E4M3: return &G_E4M3;
+    case REF_FP8_E5M2: return &G_E5M2;
     }
     return 0;
 }
@@ -174,8 +192,10 @@ double ref_code_value(int elem, int asym, int code) {
         return (double)((code & 0x8) ? (code & 0xf) - 16 : (code & 0xf));
     }
     {
-        int sbit = G->bits - 1;
-        double mag = G->g[code & ((1 << sbit) - 1)];
+        int sbit = G->bits - 1, idx = code & ((1 << sbit) - 1);
+        double mag;
+        if (idx >= G->n) return NAN;      /* FP8 Inf / NaN codes: never produced */
+        mag = G->g[idx];
         return ((code >> sbit) & 1) ? -mag : mag;
     }
 }
@@ -304,7 +324,7 @@ static int is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 static int check_format(const ref_format *f, int64_t rows, int64_t cols) {
     const grid_t *G;
     int br = f->block_rows, bc = f->block_cols;
-    if (f->elem < 0 || f->elem > REF_E3M0) return 1;
+    if (f->elem < 0 || f->elem > REF_FP8_E5M2) return 1;
     if (f->scale < 0 || f->scale > REF_SC_E3M0) return 1;
     if (f->rule < 0 || f->rule > REF_RULE_OAS) return 1;
     if (f->round < 0 || f->round > REF_CEIL) return 1;
@@ -331,13 +351,17 @@ static int check_format(const ref_format *f, int64_t rows, int64_t cols) {
 }
 
 static int64_t code_row_bytes(int elem, int64_t cols) {
+    if (elem == REF_FP8_E4M3 || elem == REF_FP8_E5M2) return cols;
     return (elem == REF_FP6_E2M3 || elem == REF_FP6_E3M2) ? cols * 3 / 4 : cols / 2;
 }
 
 /* element c of one row: 4-bit codes two per byte (even element in the low
- * nibble); 6-bit codes as a least-significant-bit-first stream */
+ * nibble); 6-bit codes as a least-significant-bit-first stream; 8-bit codes
+ * one per byte */
 static void put_code(uint8_t *row, int bits, int64_t c, int code) {
-    if (bits == 4) {
+    if (bits == 8) {
+        row[c] = (uint8_t)code;
+    } else if (bits == 4) {
         uint8_t *p = row + c / 2;
         if (c % 2 == 0) *p = (uint8_t)((*p & 0xf0) | code);
         else *p = (uint8_t)((*p & 0x0f) | (code << 4));
@@ -353,6 +377,7 @@ static void put_code(uint8_t *row, int bits, int64_t c, int code) {
 }
 
 static int get_code(const uint8_t *row, int bits, int64_t c) {
+    if (bits == 8) return row[c];
     if (bits == 4) return (c % 2 == 0) ? (row[c / 2] & 0xf) : (row[c / 2] >> 4);
     {
         int code = 0, k;

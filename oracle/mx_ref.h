@@ -19,6 +19,11 @@
  *  - the ARITH 2025 MX-training report (fmread.com academic report, "research
  *    findings"): E2M1 / INT4 / E3M0 element types, RTNE / stochastic / ceil
  *    rounding, symmetric vs asymmetric scaling, row / column / 2D blocks.
+ *  - The MX family also has 8-bit elements ("Unveiling the Potential of
+ *    Quantization with MXFP4", current state, Sec. 1 and 6: MX formats of 8,
+ *    6 and 4 bits; the proposed methods apply to MXFP8 and MXFP6).  The FP6
+ *    and FP8 element encodings themselves (E2M3, E3M2, E4M3, E5M2) are the OCP
+ *    MX definitions, which the pages build on but do not print.
  *
  * Every function takes host pointers.  Return codes: 0 ok, 1 bad argument,
  * 2 unsupported combination.
@@ -32,7 +37,8 @@ extern "C" {
 #endif
 
 /* element types */
-enum { REF_E2M1 = 0, REF_INT4 = 1, REF_FP6_E2M3 = 2, REF_FP6_E3M2 = 3, REF_E3M0 = 4 };
+enum { REF_E2M1 = 0, REF_INT4 = 1, REF_FP6_E2M3 = 2, REF_FP6_E3M2 = 3, REF_E3M0 = 4,
+       REF_FP8_E4M3 = 5, REF_FP8_E5M2 = 6 };
 /* block-scale types */
 enum { REF_SC_E8M0 = 0, REF_SC_UE4M3 = 1, REF_SC_NVFP4 = 2, REF_SC_UE5M3 = 3, REF_SC_E3M0 = 4 };
 /* power-of-two exponent rule (E8M0 scales) */

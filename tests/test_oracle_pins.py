@@ -49,6 +49,10 @@ def grid_of(ref, elem, asym=0):
         return minifloat(3, 2, 3)
     if elem == ref.INT4:
         return [Fr(i) for i in range(16 if asym else 8)]
+    if elem == ref.FP8_E4M3:       # magnitude code 0x7F is NaN
+        return minifloat(4, 3, 7)[:0x7F]
+    if elem == ref.FP8_E5M2:       # 0x7C is Inf, 0x7D-0x7F NaN
+        return minifloat(5, 2, 15)[:0x7C]
     raise ValueError(elem)
 
 
@@ -67,7 +71,8 @@ def sign_code(ref, elem, asym, neg, idx):
     return (int(neg) << (bits - 1)) | idx
 
 
-ELEMS = [("E2M1", 0, 0), ("INT4", 1, 0), ("UINT4", 1, 1), ("E2M3", 2, 0), ("E3M2", 3, 0), ("E3M0", 4, 0)]
+ELEMS = [("E2M1", 0, 0), ("INT4", 1, 0), ("UINT4", 1, 1), ("E2M3", 2, 0), ("E3M2", 3, 0), ("E3M0", 4, 0),
+         ("E4M3", 5, 0), ("E5M2", 6, 0)]
 
 
 # ---------------------------------------------------------------- formats --
@@ -89,8 +94,11 @@ def test_format_facts_from_pages(ref):
 @pytest.mark.parametrize("name,elem,asym", ELEMS)
 def test_grid_values_decode_from_bit_fields(ref, name, elem, asym):
     g = grid_of(ref, elem, asym)
-    nbits = 4 if elem in (0, 1, 4) else 6
+    nbits = 4 if elem in (0, 1, 4) else (8 if elem in (5, 6) else 6)
     for code in range(1 << nbits):
+        if nbits == 8 and (code & 0x7F) >= len(g):
+            assert math.isnan(ref.code_value(elem, asym, code))     # Inf / NaN codes
+            continue
         v = Fr(ref.code_value(elem, asym, code))
         if elem == ref.INT4:
             want = Fr(code) if asym else Fr(code - 16 if code & 8 else code)
@@ -189,7 +197,7 @@ def test_ceil_brute_force(ref, name, elem, asym):
             assert ref.round_code(elem, asym, ref.CEIL, v) == want, (name, v)
 
 
-@pytest.mark.parametrize("name,elem,asym", [e for e in ELEMS if e[0] in ("E2M1", "INT4", "E3M2")])
+@pytest.mark.parametrize("name,elem,asym", [e for e in ELEMS if e[0] in ("E2M1", "INT4", "E3M2", "E4M3", "E5M2")])
 def test_sr_exact_expectation(ref, name, elem, asym):
     """Enumerate every 16-bit draw: the mean lies in [v, v + step * 2^-16)."""
     grid = grid_of(ref, elem, asym)
@@ -664,3 +672,16 @@ def test_bad_arguments_rejected(ref):
                dict(hadamard=24), dict(macro_cols=64), dict(asymmetric=1, scale=1)):
         with pytest.raises(ValueError):
             ref.quantize(x, ref.Format(**kw))
+
+
+def test_fp8_element_grid_facts(ref):
+    """The OCP 8-bit MX element types: E4M3 max 448 = 1.75 * 2^8, smallest
+    subnormal 2^-9, 126 positive values; E5M2 max 57344 = 1.75 * 2^15, smallest
+    subnormal 2^-16; both saturate (no Inf/NaN is produced) and the FLOOR
+    rule uses emax 8 and 15."""
+    for elem, top, tiny, emax in ((ref.FP8_E4M3, 448.0, 2.0 ** -9, 8), (ref.FP8_E5M2, 57344.0, 2.0 ** -16, 15)):
+        vals = sorted({abs(v) for v in (ref.code_value(elem, 0, c) for c in range(256)) if not math.isnan(v)})
+        assert vals[-1] == top and vals[1] == tiny
+        assert ref.code_value(elem, 0, ref.round_code(elem, 0, ref.RTNE, 1e30)) == top
+        assert ref.code_value(elem, 0, ref.round_code(elem, 0, ref.RTNE, -1e30)) == -top
+        assert ref.e8m0_exponent(ref.RULE_FLOOR, 0, elem, 0, 1.0) == -emax
