@@ -67,9 +67,12 @@ extern "C" {
  *  INT4   4 bits; symmetric: -7..7 as a two's-complement nibble;
  *         asymmetric: 0..15 steps above the block offset
  *  FP6    6 bits, E2M3 (bias 1, max 7.5) or E3M2 (bias 3, max 28)
- *  E3M0   4 bits, magnitudes {0, 1/4, 1/2, 1, 2, 4, 8, 16} (exponent only)  */
+ *  E3M0   4 bits, magnitudes {0, 1/4, 1/2, 1, 2, 4, 8, 16} (exponent only)
+ *  FP8    8 bits, E4M3 (bias 7, max 448) or E5M2 (bias 15, max 57344): the
+ *         MX family's 8-bit elements ([U], current state: MX formats of 8, 6
+ *         and 4 bits); their Inf/NaN codes are never produced               */
 enum { MX_ELEM_E2M1 = 0, MX_ELEM_INT4 = 1, MX_ELEM_FP6_E2M3 = 2, MX_ELEM_FP6_E3M2 = 3,
-       MX_ELEM_E3M0 = 4 };
+       MX_ELEM_E3M0 = 4, MX_ELEM_FP8_E4M3 = 5, MX_ELEM_FP8_E5M2 = 6 };
 
 /* ---- block-scale types [U], [F], [A] ------------------------------------
  *  E8M0   one byte, the power of two 2^(code-127); 0xFF marks a block that
@@ -126,7 +129,8 @@ typedef struct mx_format {
  * memory; unused pointers may be NULL).  Layout, all row-major:
  *  codes         rows x (cols/2) bytes for 4-bit elements, element 2i in the
  *                low nibble of byte i; rows x (3*cols/4) bytes for FP6, a
- *                least-significant-bit-first stream of 6-bit codes per row
+ *                least-significant-bit-first stream of 6-bit codes per row;
+ *                rows x cols bytes for FP8, one code per byte
  *  scales        (rows/block_rows) x (cols/block_cols) bytes
  *  offsets       same grid, bf16 (asymmetric only)
  *  macro_scales  rows x (cols/128) bytes of UE4M3 (Macro Block Scaling only)
@@ -215,9 +219,10 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  * with A an M x K and B an N x K quantized tensor in row blocks along K; fp32
  * accumulation, C (M x N, row stride ldc elements) in bf16 (rounded to nearest
  * even) or fp32.  Formats, per operand:
- *  - E8M0 scales on 1 x 32 blocks (any rule) with E2M1 (MXFP4) or FP6 E2M3 /
- *    E3M2 (MXFP6) elements, chosen independently for A and B (the mixed
- *    4-/6-bit products of [A], main results): the gfx950 block-scaled
+ *  - E8M0 scales on 1 x 32 blocks (any rule) with E2M1 (MXFP4), FP6 E2M3 /
+ *    E3M2 (MXFP6) or FP8 E4M3 / E5M2 (MXFP8) elements, chosen independently
+ *    for A and B (the mixed 4-/6-bit products of [A], main results; MX also
+ *    has 8-bit formats, [U] current state): the gfx950 block-scaled
  *    FP8/FP6/FP4 matrix instruction.  MXFP4 operands may carry macro-block
  *    scales (macro_cols 128, [U] Sec. 4 MBS and Fig. 5: each 128-wide K step's
  *    partial product is multiplied by the two rows' UE4M3 macro scales).
@@ -227,7 +232,7 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  *    decoded exactly, to fp16 when both operands have UE4M3 scales and to
  *    bf16 otherwise, and the fp16 / bf16 matrix instruction multiplies.
  * Anything else (INT4 / E3M0 elements, asymmetric, rotated, column or 2D
- * blocks, macro scales on FP6): MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
+ * blocks, macro scales on FP6 / FP8): MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
  * whole blocks (MX_ERR_ARG otherwise); any M, N.  E8M0 products with K a
  * multiple of 128 run on LDS-staged kernels (MXFP4 x MXFP4 without macro
  * scales and K a multiple of 1024 on the most tuned one), other K on a

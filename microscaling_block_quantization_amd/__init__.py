@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(HERE, "libmx.so")
 
 MX_OK, MX_ERR_ARG, MX_ERR_UNSUPPORTED, MX_ERR_ALIGN, MX_ERR_WORKSPACE, MX_ERR_HIP, MX_ERR_TOO_LARGE = range(7)
 NOALLOC_SCRATCH_BYTES = 4 << 20      # MX_NOALLOC_SCRATCH_BYTES of include/mx.h
-ELEM_E2M1, ELEM_INT4, ELEM_FP6_E2M3, ELEM_FP6_E3M2, ELEM_E3M0 = range(5)
+ELEM_E2M1, ELEM_INT4, ELEM_FP6_E2M3, ELEM_FP6_E3M2, ELEM_E3M0, ELEM_FP8_E4M3, ELEM_FP8_E5M2 = range(7)
 SCALE_E8M0, SCALE_UE4M3, SCALE_NVFP4, SCALE_UE5M3, SCALE_E3M0 = range(5)
 RULE_FLOOR, RULE_CEIL, RULE_OAS = range(3)
 ROUND_RTNE, ROUND_SR, ROUND_CEIL = range(3)
@@ -132,6 +132,8 @@ class Format:
 MXFP4 = Format()
 MXFP6_E2M3 = Format(elem=ELEM_FP6_E2M3)
 MXFP6_E3M2 = Format(elem=ELEM_FP6_E3M2)
+MXFP8_E4M3 = Format(elem=ELEM_FP8_E4M3)
+MXFP8_E5M2 = Format(elem=ELEM_FP8_E5M2)
 
 
 @dataclass
@@ -293,8 +295,8 @@ def mx_qsnr(ref: torch.Tensor, approx: torch.Tensor, workspace=None, stream=None
 
 
 def mx_gemm(fa: Format, a: QTensor, fb: Format, b: QTensor, c=None, out_dtype=torch.bfloat16, stream=None):
-    """C = deq(A) . deq(B)^T for A (M x K) and B (N x K): MXFP4 or MXFP6 (E2M3 /
-    E3M2) with E8M0 scales per 1 x 32 block, in any pairing (MXFP4 operands may
+    """C = deq(A) . deq(B)^T for A (M x K) and B (N x K): MXFP4, MXFP6 (E2M3 /
+    E3M2) or MXFP8 (E4M3 / E5M2) with E8M0 scales per 1 x 32 block, in any pairing (MXFP4 operands may
     carry 1 x 128 macro-block scales, macro_cols=128); or E2M1 under UE4M3,
     NVFP4, UE5M3 or E8M0 scales on other row blocks.  c: an M x N view (any
     row stride) to write into, else a new tensor of out_dtype."""

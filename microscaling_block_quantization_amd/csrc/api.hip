@@ -25,7 +25,7 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // Validate a format for a rows x cols tensor.  Returns MX_OK or an error code.
 int check_format(const mx_format* f, int64_t rows, int64_t cols) {
     if (!f) return MX_ERR_ARG;
-    if (f->elem < 0 || f->elem > MX_ELEM_E3M0) return MX_ERR_ARG;
+    if (f->elem < 0 || f->elem > MX_ELEM_FP8_E5M2) return MX_ERR_ARG;
     if (f->scale < 0 || f->scale > MX_SCALE_E3M0) return MX_ERR_ARG;
     if (f->rule < 0 || f->rule > MX_RULE_OAS) return MX_ERR_ARG;
     if (f->round < 0 || f->round > MX_ROUND_CEIL) return MX_ERR_ARG;
@@ -62,7 +62,7 @@ int check_format(const mx_format* f, int64_t rows, int64_t cols) {
 }
 
 int64_t crow_bytes(const mx_format* f, int64_t cols) {
-    return (f->elem == MX_ELEM_FP6_E2M3 || f->elem == MX_ELEM_FP6_E3M2) ? cols * 3 / 4 : cols / 2;
+    return mxd::code_row_bytes(mxd::make_elem(f->elem, f->asymmetric).bits, cols);
 }
 
 QParams make_params(const mx_format* f, int in_bf16, const void* x, int64_t rows, int64_t cols, int64_t ld,

@@ -1,18 +1,20 @@
-// gemm_lds.hip -- LDS-staged block-scaled GEMM for MXFP6 and mixed 4-/6-bit
-// operands: C = deq(A) . deq(B)^T with E8M0 scales per 1 x 32 block and each
-// operand's elements E2M1, E2M3 or E3M2, on V_MFMA_SCALE_F32_32X32X64_F8F6F4
-// (the 6-bit and mixed products of the ARITH 2025 MX-training report, main
-// results).
+// gemm_lds.hip -- LDS-staged block-scaled GEMM for MXFP8, MXFP6 and mixed
+// 8-/6-/4-bit operands: C = deq(A) . deq(B)^T with E8M0 scales per 1 x 32
+// block and each operand's elements E2M1, E2M3, E3M2, E4M3 or E5M2, on
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 (the 6-bit and mixed products of the ARITH
+// 2025 MX-training report, main results; MX also has 8-bit elements,
+// "Unveiling the Potential of Quantization with MXFP4", current state).
 //
 // A workgroup of 8 waves (2 x 4) computes a 256 x 256 tile; each wave owns 4 x 2
 // MFMA tiles of 32 x 32.  K advances 128 per stage (two 64-wide substeps); a
-// stage holds the tile's A and B codes, 64 bytes per row for E2M1 and 96 for
-// FP6.  Three stages form a ring in LDS, filled by LDS-DMA (buffer_load ...
+// stage holds the tile's A and B codes, 64 bytes per row for E2M1, 96 for FP6
+// and 128 for FP8 (pairs with 8-bit operands use 128 x 256 or 256 x 128
+// tiles, or 256 x 256 with E2M1, so that three stages fit in LDS).  Three stages form a ring in LDS, filled by LDS-DMA (buffer_load ...
 // lds, 16 bytes per lane) two stages ahead.  The 16-byte chunks of a row are
-// permuted by a row-dependent rotation (FP6) or XOR (E2M1) so that the chunk
-// reads of 16 consecutive rows fall in distinct LDS banks.  An FP6 operand (32
-// codes, 24 bytes) spans one whole chunk and half of the next: two 16-byte
-// reads, put in order per lane.  The block scales (4 bytes per row and stage)
+// permuted by a row-dependent rotation (FP6) or XOR (E2M1, FP8) so that the
+// chunk reads of 16 consecutive rows fall in distinct LDS banks.  An FP6
+// operand (32 codes, 24 bytes) spans one whole chunk and half of the next: two
+// 16-byte reads, put in order per lane; an FP8 operand is two whole chunks.  The block scales (4 bytes per row and stage)
 // come by LDS-DMA too, in groups of 4 stages (16 bytes of a row per lane: a
 // quarter of the L2 requests of a dword per stage), so that the only loads in
 // flight in the loop are the DMA the stage waits count (and, with macro-block
@@ -31,24 +33,32 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// the instruction's type codes: FP8 E4M3 0, E5M2 1, FP6 E2M3 2, E3M2 3, FP4 E2M1 4
 constexpr int MF_E2M1 = 4;
-constexpr int lmf(int elem) { return elem == E2M1 ? 4 : elem == E2M3 ? 2 : 3; }
+constexpr int lmf(int elem) { return elem == E2M1 ? 4 : elem == E2M3 ? 2 : elem == E3M2 ? 3 : elem == E4M3 ? 0 : 1; }
+constexpr bool is_fp8(int f) { return f <= 1; }
+// bytes of one 32-element block
+constexpr int lbb(int f) { return f == MF_E2M1 ? 16 : is_fp8(f) ? 32 : 24; }
 
 template <int F>
 struct Op {
-    static constexpr int R = F == MF_E2M1 ? 64 : 96;   // bytes per row per stage
+    static constexpr int R = 4 * lbb(F);               // bytes per row per stage
     static constexpr int C = R / 16;                   // chunks per row
     // physical chunk slot of logical chunk p in tile row r, and back
     // FP6: a rotation by one slot in row quads 1 and 2 of every 16 rows; the
     // 16-byte reads of one logical chunk by 16 consecutive rows then cover 64
     // distinct banks (and those of 8 rows 32 banks)
     static __device__ __forceinline__ int rot(int r) { return ((r >> 2) & 1) ^ ((r >> 3) & 1); }
+    // FP8: 8 chunks per row, XOR by the row's low 3 bits (the 8 rows of one
+    // phase of a 16-byte read fall on 8 distinct chunk slots)
     static __device__ __forceinline__ int phys(int r, int p) {
         if constexpr (C == 4) return p ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+        else if constexpr (C == 8) return p ^ (r & 7);
         else return (p + rot(r)) % 6;
     }
     static __device__ __forceinline__ int logical(int r, int q) {
         if constexpr (C == 4) return q ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+        else if constexpr (C == 8) return q ^ (r & 7);
         else return (q + 6 - rot(r)) % 6;
     }
 };
@@ -76,11 +86,17 @@ struct LGeo {
     static constexpr int GROW = 4 * SG;
     static constexpr int GBUF = (BM + BN) * GROW;
     static constexpr int OFF_G = D * STAGE;
-    static constexpr int SMEM = OFF_G + NB * GBUF;
+    // group DMA: (BM + BN) / 64 pieces of 64 rows, GPW per wave; when they do
+    // not split evenly, the waves past the last piece load through the
+    // zero-size resource into a 1 KiB sink, so that every wave issues the
+    // same count (the stage waits count them)
+    static constexpr int GP = (BM + BN) / 64;
+    static constexpr int GPW = (GP + NW - 1) / NW;
+    static constexpr int OFF_SINK = OFF_G + NB * GBUF;
+    static constexpr int SMEM = OFF_SINK + (GP % NW ? 1024 : 0);
     static_assert(SG == 1 || SG == 4, "scale groups of 1 or 4 stages");
-    static constexpr int GPW = (BM + BN) / 64 / NW;    // group DMA pieces per wave
-    static_assert((PA + PB) % NW == 0 && (BM + BN) % (64 * NW) == 0, "DMA pieces split evenly over the waves");
-    static_assert((BM / 64) % GPW == 0, "a wave's scale pieces lie in one operand");
+    static_assert((PA + PB) % NW == 0 && (BM + BN) % 64 == 0, "code DMA pieces split evenly over the waves");
+    static_assert(GPW == 1 || (BM / 64) % GPW == 0, "a wave's scale pieces lie in one operand");
 };
 
 __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -93,7 +109,18 @@ template <int F>
 __device__ __forceinline__ v8i frag(const uint8_t* __restrict__ st, int rr, int t, int half) {
     using O = Op<F>;
     v8i v;
-    if constexpr (F == MF_E2M1) {
+    if constexpr (is_fp8(F)) {
+        // 8-bit operands are split by the instruction: the lanes of half h
+        // supply K [16h, 16h + 16) of the 64-wide step in their first four
+        // registers and K [32 + 16h, 48 + 16h) in the last four (the scale of
+        // half h still covers K [32h, 32h + 32)): chunks 4t + h and 4t + 2 + h
+        const int c = 4 * t + half;
+        const u32x4v x = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, c) * 16);
+        const u32x4v y = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, c + 2) * 16);
+        v[0] = (int)x[0]; v[1] = (int)x[1]; v[2] = (int)x[2]; v[3] = (int)x[3];
+        v[4] = (int)y[0]; v[5] = (int)y[1]; v[6] = (int)y[2]; v[7] = (int)y[3];
+        return v;
+    } else if constexpr (F == MF_E2M1) {
         const u32x4v x = *reinterpret_cast<const u32x4v*>(st + rr * O::R + O::phys(rr, 2 * t + half) * 16);
         v[0] = (int)x[0]; v[1] = (int)x[1]; v[2] = (int)x[2]; v[3] = (int)x[3];
         v[4] = 0; v[5] = 0;
@@ -250,10 +277,12 @@ __device__ __forceinline__ void group_dma(uint8_t* smem, const LPanels& P, int g
 #pragma unroll
     for (int k = 0; k < G::GPW; k++) {
         const int q = wave * G::GPW + k;                  // uniform
+        const bool real = q < G::GP;
         const bool isb = q >= G::BM / 64;
         const int row = (isb ? q - G::BM / 64 : q) * 64 + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(in ? (isb ? psb : psa) : pz, (lds_void*)(buf + q * 64 * G::GROW),
-                                                 G::GROW, row * P.kblocks + start, 0, 0, 0);
+        uint8_t* dst = real ? buf + q * 64 * G::GROW : smem + G::OFF_SINK;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(in && real ? (isb ? psb : psa) : pz, (lds_void*)dst, G::GROW,
+                                                 row * P.kblocks + start, 0, 0, 0);
     }
 #endif
 }
@@ -377,7 +406,7 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
 
     const int nst = (int)(K / G::BK);
     const int kblocks = (int)(K / 32);
-    const int64_t rowa = (int64_t)kblocks * (FA == MF_E2M1 ? 16 : 24), rowb = (int64_t)kblocks * (FB == MF_E2M1 ? 16 : 24);
+    const int64_t rowa = (int64_t)kblocks * lbb(FA), rowb = (int64_t)kblocks * lbb(FB);
     const int64_t va = M - m0 < G::BM ? M - m0 : G::BM, vb = N - n0 < G::BN ? N - n0 : G::BN;
     const rsrc_t pa = rsrc(A + m0 * rowa, va * rowa), pb = rsrc(B + n0 * rowb, vb * rowb);
     const rsrc_t psa = rsrc(SA + m0 * kblocks, va * kblocks), psb = rsrc(SB + n0 * kblocks, vb * kblocks);
@@ -444,15 +473,24 @@ hipError_t launch_lds_g(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
     return hipGetLastError();
 }
 
+// the tile of an operand pair: 256 x 256 (8 waves of 4 x 2 MFMA tiles) while
+// three stages of both operands fit in LDS; with an 8-bit operand beside a
+// 6- or 8-bit one, 128 x 256 (8-bit A) or 256 x 128 (8 waves of 2 x 2 tiles)
+template <int FA, int FB, int SG>
+struct LPick {
+    static constexpr bool big = lbb(FA) + lbb(FB) <= 48;
+    static constexpr bool tall = !big && !is_fp8(FA);       // FP6 A, FP8 B: 256 x 128
+    using G = LGeo<FA, FB, big ? LDS_WGM : (tall ? 4 : 2), big ? LDS_WGN : (tall ? 2 : 4), big ? LDS_TI : 2,
+                   big ? LDS_TJ : 2, 0, SG>;
+};
+
 // scale groups of 4 stages need K >= 512 (a whole group fits a scale row)
 template <int FA, int FB>
 hipError_t launch_lds_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, void* c, int64_t M,
                         int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
     if (K >= 512)
-        return launch_lds_g<LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ, 0, 4>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16,
-                                                                               s, nullptr, nullptr);
-    return launch_lds_g<LGeo<FA, FB, LDS_WGM, LDS_WGN, LDS_TI, LDS_TJ, 0, 1>>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s,
-                                                                           nullptr, nullptr);
+        return launch_lds_g<typename LPick<FA, FB, 4>::G>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, nullptr, nullptr);
+    return launch_lds_g<typename LPick<FA, FB, 1>::G>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s, nullptr, nullptr);
 }
 
 // MXFP4 with macro-block scales on A (MBS 1), B (2) or both (3): the same
@@ -472,7 +510,9 @@ hipError_t launch_lds_b(int eb, const uint8_t* a, const uint8_t* sa, const uint8
     switch (lmf(eb)) {
     case 4: return launch_lds_t<FA, 4>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
     case 2: return launch_lds_t<FA, 2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
-    default: return launch_lds_t<FA, 3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 3: return launch_lds_t<FA, 3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 0: return launch_lds_t<FA, 0>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    default: return launch_lds_t<FA, 1>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
     }
 }
 
@@ -492,7 +532,9 @@ hipError_t launch_gemm_lds(int ea, const uint8_t* a, const uint8_t* sa, int eb, 
     switch (lmf(ea)) {
     case 4: return launch_lds_b<4>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
     case 2: return launch_lds_b<2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
-    default: return launch_lds_b<3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 3: return launch_lds_b<3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    case 0: return launch_lds_b<0>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
+    default: return launch_lds_b<1>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s);
     }
 }
 

@@ -30,17 +30,20 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int TM = 128, TN = 128, TK = 128;
 
 // Element formats of the matrix instruction's type fields (CBSZ for A, BLGP for
-// B): FP6 E2M3, FP6 E3M2, FP4 E2M1.  The library's own element enumeration
-// differs; fmt_of() maps it.
-constexpr int MF_E2M3 = 2, MF_E3M2 = 3, MF_E2M1 = 4;
-constexpr int fmt_of(int elem) { return elem == E2M1 ? MF_E2M1 : elem == E2M3 ? MF_E2M3 : MF_E3M2; }
-// bytes of one 32-element block: 16 for E2M1, 24 for FP6
-constexpr int block_bytes(int mf) { return mf == MF_E2M1 ? 16 : 24; }
+// B): FP8 E4M3, FP8 E5M2, FP6 E2M3, FP6 E3M2, FP4 E2M1.  The library's own
+// element enumeration differs; fmt_of() maps it.
+constexpr int MF_E4M3 = 0, MF_E5M2 = 1, MF_E2M3 = 2, MF_E3M2 = 3, MF_E2M1 = 4;
+constexpr int fmt_of(int elem) {
+    return elem == E2M1 ? MF_E2M1 : elem == E2M3 ? MF_E2M3 : elem == E3M2 ? MF_E3M2 : elem == E4M3 ? MF_E4M3 : MF_E5M2;
+}
+// bytes of one 32-element block: 16 for E2M1, 24 for FP6, 32 for FP8
+constexpr int block_bytes(int mf) { return mf == MF_E2M1 ? 16 : mf >= MF_E2M3 ? 24 : 32; }
 
-// one lane's operand: the 32 codes of one block as the format packs them (two
-// E2M1 codes per byte, low nibble first; FP6 as a 6-bit stream from the low
-// bit of the first byte), which is the instruction's operand layout for that
-// type: four registers for E2M1, six for FP6.  p is 8-byte aligned.
+// one lane's 4- or 6-bit operand: the 32 codes of one block as the format
+// packs them (two E2M1 codes per byte, low nibble first; FP6 as a 6-bit stream
+// from the low bit of the first byte), which is the instruction's operand
+// layout for those types: four registers for E2M1, six for FP6 (8-bit
+// operands: load_fp8_step).  p is 8-byte aligned.
 template <int MF>
 __device__ __forceinline__ v8i load_block(const uint8_t* p) {
     v8i v;
@@ -56,6 +59,23 @@ __device__ __forceinline__ v8i load_block(const uint8_t* p) {
     }
     return v;
 }
+// an 8-bit operand of the 64-wide K step that starts at byte `step` of row p:
+// the instruction takes K [16h, 16h + 16) of the step in the first four
+// registers of the lanes of half h and K [32 + 16h, 48 + 16h) in the last four
+// (the scale of half h still covers K [32h, 32h + 32)); a 16-byte piece past
+// the end of K (nb blocks in the row) reads as zero
+__device__ __forceinline__ v8i load_fp8_step(const uint8_t* p, int64_t step, int half, int64_t nb) {
+    v8i v;
+    const int64_t b0 = step / 32;                 // the step's first 32-element block
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const bool in = b0 + q < nb;
+        const uint4 w = in ? *reinterpret_cast<const uint4*>(p + step + 32 * q + 16 * half) : make_uint4(0, 0, 0, 0);
+        v[4 * q] = (int)w.x; v[4 * q + 1] = (int)w.y; v[4 * q + 2] = (int)w.z; v[4 * q + 3] = (int)w.w;
+    }
+    return v;
+}
+
 __device__ __forceinline__ v8i zero_block() {
     v8i v;
 #pragma unroll
@@ -103,8 +123,11 @@ __global__ __launch_bounds__(256) void k_gemm_simple(const uint8_t* __restrict__
             for (int kk = 0; kk < 2; kk++) {
                 const int64_t kb = k0 / 32 + 2 * kk + half;   // this lane's K block
                 const bool in = kb < kblocks;
-                av[i][kk] = in ? load_block<FA>(A + ra[i] * rowa + kb * block_bytes(FA)) : zero_block();
-                bv[i][kk] = in ? load_block<FB>(B + rb[i] * rowb + kb * block_bytes(FB)) : zero_block();
+                const int64_t kb0 = k0 / 32 + 2 * kk;           // the step's first block
+                if constexpr (FA == MF_E4M3 || FA == MF_E5M2) av[i][kk] = load_fp8_step(A + ra[i] * rowa, kb0 * 32, half, kblocks);
+                else av[i][kk] = in ? load_block<FA>(A + ra[i] * rowa + kb * block_bytes(FA)) : zero_block();
+                if constexpr (FB == MF_E4M3 || FB == MF_E5M2) bv[i][kk] = load_fp8_step(B + rb[i] * rowb, kb0 * 32, half, kblocks);
+                else bv[i][kk] = in ? load_block<FB>(B + rb[i] * rowb + kb * block_bytes(FB)) : zero_block();
                 ca[kk] = in ? SA[ra[i] * kblocks + kb] : 0u;
                 cb[kk] = in ? SB[rb[i] * kblocks + kb] : 0u;
             }
@@ -714,13 +737,15 @@ void launch_simple_b(int eb, const uint8_t* a, const uint8_t* sa, const uint8_t*
     switch (fmt_of(eb)) {
     case MF_E2M1: launch_simple<FA, MF_E2M1>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
     case MF_E2M3: launch_simple<FA, MF_E2M3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
-    default: launch_simple<FA, MF_E3M2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E3M2: launch_simple<FA, MF_E3M2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E4M3: launch_simple<FA, MF_E4M3>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    default: launch_simple<FA, MF_E5M2>(a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
     }
 }
 
 }  // namespace
 
-bool gemm_elem_ok(int elem) { return elem == E2M1 || elem == E2M3 || elem == E3M2; }
+bool gemm_elem_ok(int elem) { return elem == E2M1 || elem == E2M3 || elem == E3M2 || elem == E4M3 || elem == E5M2; }
 
 hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, const uint8_t* b, const uint8_t* sb,
                        void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
@@ -764,7 +789,9 @@ hipError_t launch_gemm(int ea, const uint8_t* a, const uint8_t* sa, int eb, cons
     switch (fmt_of(ea)) {
     case MF_E2M1: launch_simple_b<MF_E2M1>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
     case MF_E2M3: launch_simple_b<MF_E2M3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
-    default: launch_simple_b<MF_E3M2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E3M2: launch_simple_b<MF_E3M2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    case MF_E4M3: launch_simple_b<MF_E4M3>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
+    default: launch_simple_b<MF_E5M2>(eb, a, sa, b, sb, c, M, N, K, ldc, c_bf16, s); break;
     }
     return hipGetLastError();
 }

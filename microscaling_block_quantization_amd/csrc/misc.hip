@@ -68,6 +68,7 @@ __global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64
 }
 
 __device__ __forceinline__ int read_code(const uint8_t* row, int bits, int64_t c) {
+    if (bits == 8) return row[c];
     if (bits == 4) return (row[c >> 1] >> ((c & 1) * 4)) & 0xf;
     const int64_t bit = 6 * c;
     // the second byte is read only when the code crosses into it, so the last
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(NT) void k_dequant(QParams p, void* y, int64_t ld, 
     const int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x;
     if (q >= p.rows * per_row) return;
     const int64_t r = q / per_row, c0 = (q - r * per_row) * 8;
-    const int64_t crow = E.bits == 4 ? p.cols / 2 : p.cols * 3 / 4;
+    const int64_t crow = code_row_bytes(E.bits, p.cols);
     const uint8_t* row = p.codes + r * crow;
     const float g = p.scale == SC_NVFP4 ? *p.tensor_scale : 1.0f;
     const int eref = p.scale == SC_E3M0 ? *p.ref_exp : 0;

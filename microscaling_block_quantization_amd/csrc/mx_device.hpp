@@ -15,7 +15,7 @@
 
 namespace mxd {
 
-enum { E2M1 = 0, INT4 = 1, E2M3 = 2, E3M2 = 3, E3M0 = 4 };
+enum { E2M1 = 0, INT4 = 1, E2M3 = 2, E3M2 = 3, E3M0 = 4, E4M3 = 5, E5M2 = 6 };
 enum { SC_E8M0 = 0, SC_UE4M3 = 1, SC_NVFP4 = 2, SC_UE5M3 = 3, SC_E3M0 = 4 };
 enum { RULE_FLOOR = 0, RULE_CEIL = 1, RULE_OAS = 2 };
 enum { RTNE = 0, SR = 1, CEILR = 2 };
@@ -60,7 +60,7 @@ __device__ __forceinline__ int e_ceil(float a, float Q) {
 struct Elem {
     int kind;       // E2M1 ... E3M0
     int asym;       // INT4 min/max variant
-    int bits;       // 4 or 6
+    int bits;       // 4, 6 or 8
     float qmax;     // largest magnitude
     int emax;       // floor(log2(qmax))
     int maxidx;     // largest magnitude index
@@ -70,12 +70,15 @@ __host__ __device__ inline Elem make_elem(int kind, int asym) {
     Elem e;
     e.kind = kind;
     e.asym = asym;
-    e.bits = (kind == E2M3 || kind == E3M2) ? 6 : 4;
+    e.bits = (kind == E2M3 || kind == E3M2) ? 6 : (kind == E4M3 || kind == E5M2) ? 8 : 4;
     switch (kind) {
     case E2M1: e.qmax = 6.f; e.emax = 2; e.maxidx = 7; break;
     case INT4: e.qmax = asym ? 15.f : 7.f; e.emax = asym ? 3 : 2; e.maxidx = asym ? 15 : 7; break;
     case E2M3: e.qmax = 7.5f; e.emax = 2; e.maxidx = 31; break;
     case E3M2: e.qmax = 28.f; e.emax = 4; e.maxidx = 31; break;
+    // FP8 (OCP): E4M3 magnitude 0x7F is NaN, E5M2 0x7C is Inf; both saturate
+    case E4M3: e.qmax = 448.f; e.emax = 8; e.maxidx = 0x7e; break;
+    case E5M2: e.qmax = 57344.f; e.emax = 15; e.maxidx = 0x7b; break;
     default: e.qmax = 16.f; e.emax = 4; e.maxidx = 7; break;  // E3M0
     }
     return e;
@@ -109,6 +112,8 @@ __device__ __forceinline__ int grid_index(const Elem& E, float m, bool nearest) 
     case E2M1: i = mf_index<1, 1>(m, nearest); break;
     case E2M3: i = mf_index<3, 1>(m, nearest); break;
     case E3M2: i = mf_index<2, 3>(m, nearest); break;
+    case E4M3: i = mf_index<3, 7>(m, nearest); break;
+    case E5M2: i = mf_index<2, 15>(m, nearest); break;
     case INT4: {
         float r = nearest ? rintf(m) : floorf(m);
         i = (int)fminf(r, (float)E.maxidx);
@@ -133,6 +138,8 @@ __device__ __forceinline__ float grid_value(const Elem& E, int idx) {
     case E2M1: return mf_value<1, 1>(idx);
     case E2M3: return mf_value<3, 1>(idx);
     case E3M2: return mf_value<2, 3>(idx);
+    case E4M3: return mf_value<3, 7>(idx);
+    case E5M2: return mf_value<2, 15>(idx);
     case INT4: return (float)idx;
     default: return idx == 0 ? 0.f : bitsf((uint32_t)(idx + 124) << 23);
     }
@@ -161,6 +168,12 @@ __device__ __forceinline__ int encode(const Elem& E, int mode, float v, uint32_t
     }
     if (E.kind == INT4) return E.asym ? idx : ((neg ? -idx : idx) & 0xf);
     return ((int)neg << (E.bits - 1)) | idx;
+}
+
+// bytes of one row of codes: 4-bit codes two per byte, 6-bit codes as a
+// bit stream (4 per 3 bytes), 8-bit codes one per byte
+__host__ __device__ inline int64_t code_row_bytes(int bits, int64_t cols) {
+    return bits == 8 ? cols : bits == 6 ? cols * 3 / 4 : cols / 2;
 }
 
 __device__ __forceinline__ float decode(const Elem& E, int code) {

@@ -86,7 +86,14 @@ __device__ __forceinline__ void hadamard(float (&x)[CH], int h) {
 }
 
 __device__ __forceinline__ void store_codes(uint8_t* row, int bits, int64_t c0, const int* code, int n) {
-    if (bits == 4) {
+    if (bits == 8) {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            if (i < n) w[i >> 2] |= (uint32_t)(code[i] & 0xff) << (8 * (i & 3));
+        if (n == 16) *reinterpret_cast<uint4*>(row + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+        else *reinterpret_cast<uint2*>(row + c0) = make_uint2(w[0], w[1]);
+    } else if (bits == 4) {
         if (n == 16) {
             uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
     }
 
     if (active) {
-        store_codes(p.codes + r * (E.bits == 4 ? p.cols / 2 : p.cols * 3 / 4), E.bits, c0, code, CH);
+        store_codes(p.codes + r * code_row_bytes(E.bits, p.cols), E.bits, c0, code, CH);
         if (p.dq) store_dq<CH>(p, r, c0, d);
     }
     if (p.parts) {

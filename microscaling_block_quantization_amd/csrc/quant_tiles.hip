@@ -3,13 +3,23 @@
 // MX-training report, main results 5: column blocks for activations, 2D blocks
 // as the balance).
 //
-// One thread owns V consecutive columns (one 16-byte load per row: 8 bf16 or
-// 4 fp32) of one b-row band and keeps the b rows in registers as raw words,
-// so the band is read from HBM once and every load of a wave is a coalesced
-// 1 KiB row segment.  Column maxima reduce inside the thread; a 2D block
-// spans b/V neighbouring lanes that combine their maxima by shuffles.  Codes
-// stay row-major (element (r, c) at the same place as for row blocks), so the
-// down-column reduction never needs a transposed store.
+// A workgroup owns a band of b rows and 1 KiB of each of them (512 bf16 or 256
+// fp32 columns) and stages it in LDS with coalesced 16-byte loads: every load
+// of a wave is one 1 KiB row segment.  Then
+//  pass 1  each thread reduces its columns (two bf16 columns, or one fp32
+//          column: one LDS word per row) down the b rows; the lanes of a 2D
+//          block combine their maxima by shuffles.  The block's scale goes to
+//          memory and, packed with the kind of scaling and the offset, into an
+//          LDS parameter word per column;
+//  pass 2  each thread re-reads 16-byte row chunks of the band from LDS,
+//          rounds them with their columns' parameters and writes codes and
+//          dequantized values row-major, so every store of a wave is
+//          coalesced as well.
+// Codes keep the row-block layout (element (r, c) where a row block puts it);
+// the scale grid is (rows / b) x (cols / bc).  Statistics accumulate per
+// chunk in fp32 (float64 when a chunk's sums leave the fp32 range) and per
+// thread in float64; a block counts as all-zero when every dequantized value
+// of it is zero, which the chunks record in an LDS bit mask per column.
 #include "mx_kernels.hpp"
 
 namespace mxk {
@@ -17,145 +27,192 @@ using namespace mxd;
 
 namespace {
 
+constexpr int TROW = 1024;                     // bytes of one band row in LDS
+
+// kinds of block scaling, in the LDS parameter word of a column
+enum { K_POW2 = 0, K_DIV = 1, K_ZERO = 2, K_NAN = 3 };
+
+__device__ __forceinline__ uint32_t pack_prm(int code, int kind, uint16_t off) {
+    return (uint32_t)(code & 0xff) | ((uint32_t)kind << 8) | ((uint32_t)off << 16);
+}
+
 template <bool BF>
-__device__ __forceinline__ float word_elem(const uint32_t* w, int i) {
-    if constexpr (BF) return (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
-    else return __uint_as_float(w[i]);
+__device__ __forceinline__ float word_elem(uint32_t w, int j) {
+    if constexpr (BF) return j ? bf16hi(w) : bf16lo(w);
+    else return __uint_as_float(w);
 }
 
 template <bool BF, int BR>
 __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
-    constexpr int V = BF ? 8 : 4;          // columns per thread
+    constexpr int CPT = BF ? 2 : 1;            // columns per thread in pass 1
+    constexpr int TC = TROW / (BF ? 2 : 4);    // columns of the tile
+    constexpr int EPC = BF ? 8 : 4;            // elements per 16-byte chunk
+    constexpr int NCH = BR * (TROW / 16);      // chunks of the band
+    __shared__ __attribute__((aligned(16))) uint8_t tile[BR * TROW];
+    __shared__ __attribute__((aligned(16))) uint32_t prm[TC];
+    __shared__ uint32_t zmask[TC / 32];
+
     const Elem E = make_elem(p.elem, p.asym);
-    const int64_t vpr = p.cols / V;         // thread columns per band
-    const int64_t total = (p.rows / BR) * vpr;
-    const int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x;
-    const bool active = q < total;
-    const int64_t band = active ? q / vpr : 0;
-    const int64_t c0 = active ? (q - band * vpr) * V : 0;
+    const int tid = threadIdx.x;
+    const int64_t ctiles = (p.cols + TC - 1) / TC;
+    const int64_t band = blockIdx.x / ctiles;
+    const int64_t col0 = (blockIdx.x - band * ctiles) * TC;
     const int64_t r0 = band * BR;
+    const int ncol = (int)(p.cols - col0 < TC ? p.cols - col0 : TC);   // a multiple of 8 and of bc
+    const char* xin = static_cast<const char*>(p.x);
+
+    // ---- stage the band: chunk k is row k / 64, 16-byte piece k % 64 -------
+#pragma unroll
+    for (int k = tid; k < NCH; k += NT) {
+        const int row = k >> 6, pc = k & 63;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (pc * EPC < ncol) w = ld_stream16(xin + ((r0 + row) * p.ld + col0 + pc * EPC) * (BF ? 2 : 4));
+        *reinterpret_cast<u32x4*>(tile + row * TROW + pc * 16) = w;
+    }
+    if (tid < TC / 32) zmask[tid] = ~0u;
+    __syncthreads();
+
     const bool two_d = p.bc > 1;
-    const int G = two_d ? (BR / V > 0 ? BR / V : 1) : 1;
-    const bool leader = (threadIdx.x % G) == 0;
-
-    uint32_t w[BR][4];
-#pragma unroll
-    for (int rr = 0; rr < BR; rr++) {
-        if (active) {
-            u32x4 t = ld_stream16(static_cast<const uint8_t*>(p.x) + ((r0 + rr) * p.ld + c0) * (BF ? 2 : 4));
-            w[rr][0] = t.x; w[rr][1] = t.y; w[rr][2] = t.z; w[rr][3] = t.w;
-        } else {
-            w[rr][0] = w[rr][1] = w[rr][2] = w[rr][3] = 0;
-        }
-    }
-
-    // per column statistics over the band
-    float amax[V], mn[V], mx[V];
-    int fin[V];
-#pragma unroll
-    for (int j = 0; j < V; j++) { amax[j] = 0.f; mn[j] = INFINITY; mx[j] = -INFINITY; fin[j] = 1; }
-#pragma unroll
-    for (int rr = 0; rr < BR; rr++) {
-#pragma unroll
-        for (int j = 0; j < V; j++) {
-            float v = word_elem<BF>(w[rr], j);
-            if (!finitef(v)) { fin[j] = 0; continue; }
-            amax[j] = fmaxf(amax[j], fabsf(v));
-            mn[j] = fminf(mn[j], v);
-            mx[j] = fmaxf(mx[j], v);
-        }
-    }
-    if (two_d) {
-        // one block covers all V columns of this thread and G - 1 neighbours
-        float a = amax[0], lo = mn[0], hi = mx[0];
-        int f = fin[0];
-#pragma unroll
-        for (int j = 1; j < V; j++) { a = fmaxf(a, amax[j]); lo = fminf(lo, mn[j]); hi = fmaxf(hi, mx[j]); f &= fin[j]; }
-        a = group_max_rt(a, G);
-        f = group_and_rt(f, G);
-        if (p.asym) { lo = group_min_rt(lo, G); hi = group_max_rt(hi, G); }
-#pragma unroll
-        for (int j = 0; j < V; j++) { amax[j] = a; mn[j] = lo; mx[j] = hi; fin[j] = f; }
-    }
-
+    constexpr int G1 = BR / CPT;               // lanes of one 2D block in pass 1
     const float g = (p.scale == SC_NVFP4) ? *p.tensor_scale : 1.0f;
     const int eref = (p.scale == SC_E3M0) ? *p.ref_exp : 0;
     const bool ue5 = p.scale == SC_UE5M3;
 
-    int kind[V], e[V], sc[V];
-    float S[V], sb[V], o[V];
-    uint16_t ob[V];
+    // ---- pass 1: block maxima and scales -------------------------------------
+    {
+        float amax[CPT], mn[CPT], mx[CPT];
+        int fin[CPT];
 #pragma unroll
-    for (int j = 0; j < V; j++) {
-        kind[j] = 0; e[j] = 0; sc[j] = 0; S[j] = 1.f; sb[j] = 1.f; o[j] = 0.f; ob[j] = 0;
-        if (!fin[j]) {
-            kind[j] = 3;
-            sc[j] = (p.scale == SC_UE4M3 || p.scale == SC_NVFP4) ? 0x7f : 0xff;
-        } else if (p.asym) {
-            if (E.kind == INT4) {
-                ob[j] = bf16_floor(mn[j]);
-                o[j] = bf16f(ob[j]);
-                float R = mx[j] - o[j];
-                e[j] = R > 0.f ? e8m0_exp(p.rule, p.tau, E, R) : -127;
-            } else {
-                // the mid-range, each end halved first so that it cannot overflow
-                ob[j] = bf16_rne(mx[j] * 0.5f + mn[j] * 0.5f);
-                o[j] = bf16f(ob[j]);
+        for (int j = 0; j < CPT; j++) { amax[j] = 0.f; mn[j] = INFINITY; mx[j] = -INFINITY; fin[j] = 1; }
+#pragma unroll
+        for (int row = 0; row < BR; row++) {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(tile + row * TROW)[tid];
+#pragma unroll
+            for (int j = 0; j < CPT; j++) {
+                const float v = word_elem<BF>(w, j);
+                if (!finitef(v)) { fin[j] = 0; continue; }
+                amax[j] = fmaxf(amax[j], fabsf(v));
+                mn[j] = fminf(mn[j], v);
+                mx[j] = fmaxf(mx[j], v);
             }
-        } else if (p.scale == SC_E8M0) {
-            e[j] = e8m0_exp(p.rule, p.tau, E, amax[j]);
-        } else if (p.scale == SC_E3M0) {
-            int cdown = 7;
-            if (amax[j] > 0.f) {
-                cdown = eref - e_ceil(amax[j], E.qmax);
-                cdown = cdown < 0 ? 0 : (cdown > 7 ? 7 : cdown);
-            }
-            e[j] = eref - cdown;
-            sc[j] = cdown;
-        } else {
-            float t = amax[j] / E.qmax;
-            if (p.scale == SC_NVFP4) t = t / g;
-            sc[j] = fp8_code(ue5, t);
-            sb[j] = fp8_value(ue5, sc[j]);
-            S[j] = (p.scale == SC_NVFP4) ? sb[j] * g : sb[j];
-            kind[j] = (S[j] == 0.f) ? 2 : 1;
         }
-    }
-    if (p.asym && E.kind != INT4) {
-        // E2M1 with offset: the exponent comes from max |x - o| over the block
-        float ym[V];
-#pragma unroll
-        for (int j = 0; j < V; j++) ym[j] = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < BR; rr++)
-#pragma unroll
-            for (int j = 0; j < V; j++) ym[j] = fmaxf(ym[j], fabsf(word_elem<BF>(w[rr], j) - o[j]));
         if (two_d) {
-            float a = ym[0];
+            float a = amax[0], lo = mn[0], hi = mx[0];
+            int f = fin[0];
 #pragma unroll
-            for (int j = 1; j < V; j++) a = fmaxf(a, ym[j]);
-            a = group_max_rt(a, G);
+            for (int j = 1; j < CPT; j++) { a = fmaxf(a, amax[j]); lo = fminf(lo, mn[j]); hi = fmaxf(hi, mx[j]); f &= fin[j]; }
+            a = group_max<G1>(a);
+            f = group_and<G1>(f);
+            lo = group_min<G1>(lo);
+            hi = group_max<G1>(hi);
 #pragma unroll
-            for (int j = 0; j < V; j++) ym[j] = a;
+            for (int j = 0; j < CPT; j++) { amax[j] = a; mn[j] = lo; mx[j] = hi; fin[j] = f; }
+        }
+        int kind[CPT], e[CPT], sc[CPT];
+        uint16_t ob[CPT];
+        float o[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; j++) {
+            kind[j] = K_POW2; e[j] = 0; sc[j] = 0; ob[j] = 0; o[j] = 0.f;
+            if (!fin[j]) {
+                kind[j] = K_NAN;
+                sc[j] = (p.scale == SC_UE4M3 || p.scale == SC_NVFP4) ? 0x7f : 0xff;
+            } else if (p.asym) {
+                if (E.kind == INT4) {
+                    ob[j] = bf16_floor(mn[j]);
+                    o[j] = bf16f(ob[j]);
+                    const float R = mx[j] - o[j];
+                    e[j] = R > 0.f ? e8m0_exp(p.rule, p.tau, E, R) : -127;
+                } else {
+                    // the mid-range, each end halved first so that it cannot overflow
+                    ob[j] = bf16_rne(mx[j] * 0.5f + mn[j] * 0.5f);
+                    o[j] = bf16f(ob[j]);
+                }
+            } else if (p.scale == SC_E8M0) {
+                e[j] = e8m0_exp(p.rule, p.tau, E, amax[j]);
+            } else if (p.scale == SC_E3M0) {
+                int cdown = 7;
+                if (amax[j] > 0.f) {
+                    cdown = eref - e_ceil(amax[j], E.qmax);
+                    cdown = cdown < 0 ? 0 : (cdown > 7 ? 7 : cdown);
+                }
+                e[j] = eref - cdown;
+                sc[j] = cdown;
+            } else {
+                float t = amax[j] / E.qmax;
+                if (p.scale == SC_NVFP4) t = t / g;
+                sc[j] = fp8_code(ue5, t);
+                const float sbv = fp8_value(ue5, sc[j]);
+                kind[j] = ((p.scale == SC_NVFP4 ? sbv * g : sbv) == 0.f) ? K_ZERO : K_DIV;
+            }
+        }
+        if (p.asym && E.kind != INT4) {
+            // E2M1 with an offset: the exponent comes from max |x - o| over the block
+            float ym[CPT];
+#pragma unroll
+            for (int j = 0; j < CPT; j++) ym[j] = 0.f;
+#pragma unroll
+            for (int row = 0; row < BR; row++) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(tile + row * TROW)[tid];
+#pragma unroll
+                for (int j = 0; j < CPT; j++) ym[j] = fmaxf(ym[j], fabsf(word_elem<BF>(w, j) - o[j]));
+            }
+            if (two_d) {
+                float a = ym[0];
+#pragma unroll
+                for (int j = 1; j < CPT; j++) a = fmaxf(a, ym[j]);
+                a = group_max<G1>(a);
+#pragma unroll
+                for (int j = 0; j < CPT; j++) ym[j] = a;
+            }
+#pragma unroll
+            for (int j = 0; j < CPT; j++)
+                if (kind[j] == K_POW2) e[j] = e8m0_exp(p.rule, p.tau, E, ym[j]);
         }
 #pragma unroll
-        for (int j = 0; j < V; j++)
-            if (kind[j] == 0) e[j] = e8m0_exp(p.rule, p.tau, E, ym[j]);
-    }
+        for (int j = 0; j < CPT; j++) {
+            // the E8M0 code of a power-of-two scale (E3M0 keeps its step-down
+            // code; pass 2 rebuilds e from it)
+            if (kind[j] == K_POW2 && p.scale != SC_E3M0) sc[j] = e[j] + 127;
+            prm[tid * CPT + j] = pack_prm(sc[j], kind[j], kind[j] == K_NAN ? (uint16_t)0 : ob[j]);
+        }
+        const int col = tid * CPT;
+        if (col < ncol) {
+            if (two_d) {
+                if (tid % G1 == 0) {
+                    const int64_t sidx = band * (p.cols / BR) + (col0 + col) / BR;
+                    p.scales[sidx] = (uint8_t)sc[0];
+                    if (p.asym) p.offsets[sidx] = kind[0] == K_NAN ? (uint16_t)0 : ob[0];
+                }
+            } else {
 #pragma unroll
-    for (int j = 0; j < V; j++)
-        if (kind[j] != 3 && (p.scale == SC_E8M0 || p.asym)) sc[j] = e[j] + 127;
+                for (int j = 0; j < CPT; j++) {
+                    const int64_t sidx = band * p.cols + col0 + col + j;
+                    p.scales[sidx] = (uint8_t)sc[j];
+                    if (p.asym) p.offsets[sidx] = kind[j] == K_NAN ? (uint16_t)0 : ob[j];
+                }
+            }
+        }
+    }
+    __syncthreads();
 
+    // ---- pass 2: round, store codes and dequantized values, statistics --------
     double s2 = 0, e2 = 0;
     unsigned long long nz = 0, fl = 0, zb = 0;
-    int allzero[V];
+    const int64_t crow = code_row_bytes(E.bits, p.cols);
+#pragma unroll 1
+    for (int k = tid; k < NCH; k += NT) {
+        const int row = k >> 6, pc = k & 63;
+        const int cl = pc * EPC;                  // first column of the chunk in the tile
+        if (cl >= ncol) continue;
+        const int64_t r = r0 + row, c0 = col0 + cl;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + row * TROW + pc * 16);
+        uint32_t pr[EPC];
 #pragma unroll
-    for (int j = 0; j < V; j++) allzero[j] = 1;
-    const int64_t crow = (E.bits == 4) ? p.cols / 2 : p.cols * 3 / 4;
-
-#pragma unroll
-    for (int rr = 0; rr < BR; rr++) {
-        const int64_t r = r0 + rr;
+        for (int q = 0; q < EPC / 4; q++) {
+            const u32x4 t = *reinterpret_cast<const u32x4*>(prm + cl + 4 * q);
+            pr[4 * q] = t.x; pr[4 * q + 1] = t.y; pr[4 * q + 2] = t.z; pr[4 * q + 3] = t.w;
+        }
         uint32_t rnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (p.round == SR) {
             const uint64_t idx = (uint64_t)(r * p.cols + c0);
@@ -164,105 +221,132 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                 rnd[0] = rnd[4]; rnd[1] = rnd[5]; rnd[2] = rnd[6]; rnd[3] = rnd[7];
             }
         }
-        int code[V];
-        float d[V];
+        int code[EPC];
+        float d[EPC], xs[EPC];
+        uint32_t nzmask = 0;
 #pragma unroll
-        for (int j = 0; j < V; j++) {
-            const float xv = word_elem<BF>(w[rr], j);
+        for (int j = 0; j < EPC; j++) {
+            const float xv = BF ? word_elem<true>(w[j >> 1], j & 1) : __uint_as_float(w[j]);
+            const int sc = (int)(pr[j] & 0xff), kind = (int)((pr[j] >> 8) & 0xff);
             int c;
             float dv;
-            if (kind[j] == 3) {
+            if (kind == K_NAN) {
                 c = 0;
                 dv = __uint_as_float(0x7fc00000u);
+            } else if (kind == K_POW2) {
+                const int e = p.scale == SC_E3M0 ? eref - sc : sc - 127;
+                const float o = bf16f((uint16_t)(pr[j] >> 16));
+                const float v = (p.asym ? (xv - o) : xv) * pow2f(-e);
+                c = encode(E, p.round, v, rnd[j]);
+                dv = decode(E, c) * pow2f(e);
+                if (p.asym) dv = dv + o;
             } else {
-                float v;
-                if (kind[j] == 0) v = (p.asym ? (xv - o[j]) : xv) * pow2f(-e[j]);
-                else if (kind[j] == 1) v = xv / S[j];
-                else v = (fbits(xv) >> 31) ? -0.f : 0.f;
-                c = encode(E, kind[j] == 2 ? RTNE : p.round, v, rnd[j]);
-                float val = decode(E, c);
-                if (kind[j] == 0) {
-                    dv = val * pow2f(e[j]);
-                    if (p.asym) dv = dv + o[j];
-                } else {
-                    dv = val * sb[j];
-                    if (p.scale == SC_NVFP4) dv = dv * g;
-                }
+                const float sb = fp8_value(ue5, sc);
+                const float S = p.scale == SC_NVFP4 ? sb * g : sb;
+                const float v = kind == K_ZERO ? ((fbits(xv) >> 31) ? -0.f : 0.f) : xv / S;
+                c = encode(E, kind == K_ZERO ? RTNE : p.round, v, rnd[j]);
+                dv = decode(E, c) * sb;
+                if (p.scale == SC_NVFP4) dv = dv * g;
             }
             code[j] = c;
             d[j] = dv;
-            allzero[j] &= (dv == 0.f);
-            if (active && p.parts) {
-                double xd = xv, dd = dv;
-                s2 += xd * xd;
-                e2 += (xd - dd) * (xd - dd);
-                nz += (xv != 0.f);
-                fl += (xv != 0.f && dv == 0.f);
+            xs[j] = xv;
+            nzmask |= (dv != 0.f ? 1u : 0u) << j;
+        }
+        if (nzmask) atomicAnd(&zmask[cl >> 5], ~(nzmask << (cl & 31)));
+        if (p.parts) {
+            float s2c = 0.f, e2c = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPC; j++) {
+                const float rj = xs[j] - d[j];
+                s2c = __builtin_fmaf(xs[j], xs[j], s2c);
+                e2c = __builtin_fmaf(rj, rj, e2c);
+                nz += (xs[j] != 0.f);
+                fl += (xs[j] != 0.f && d[j] == 0.f);
+            }
+            if (fabsf(s2c) < INFINITY && fabsf(e2c) < INFINITY) {
+                s2 += (double)s2c;
+                e2 += (double)e2c;
+            } else {
+                // a square beyond the fp32 range (or a NaN): this chunk in float64
+#pragma unroll
+                for (int j = 0; j < EPC; j++) {
+                    const double xd = xs[j], dd = d[j];
+                    s2 += xd * xd;
+                    e2 += (xd - dd) * (xd - dd);
+                }
             }
         }
-        if (active) {
-            uint8_t* row = p.codes + r * crow;
-            if (E.bits == 4) {
-                uint32_t word = 0;
+        uint8_t* crw = p.codes + r * crow;
+        if (E.bits == 4) {
+            uint32_t word = 0;
 #pragma unroll
-                for (int j = 0; j < V; j++) word |= (uint32_t)code[j] << (4 * j);
-                if (V == 8) *reinterpret_cast<uint32_t*>(row + c0 / 2) = word;
-                else *reinterpret_cast<uint16_t*>(row + c0 / 2) = (uint16_t)word;
+            for (int j = 0; j < EPC; j++) word |= (uint32_t)(code[j] & 0xf) << (4 * j);
+            if constexpr (BF) *reinterpret_cast<uint32_t*>(crw + c0 / 2) = word;
+            else *reinterpret_cast<uint16_t*>(crw + c0 / 2) = (uint16_t)word;
+        } else if (E.bits == 6) {
+            uint64_t bw = 0;
+#pragma unroll
+            for (int j = 0; j < EPC; j++) bw |= (uint64_t)(code[j] & 0x3f) << (6 * j);
+            uint8_t* dst = crw + c0 * 3 / 4;
+            if constexpr (BF) {
+                uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+                d16[0] = (uint16_t)bw; d16[1] = (uint16_t)(bw >> 16); d16[2] = (uint16_t)(bw >> 32);
             } else {
-                uint64_t bitsw = 0;
-#pragma unroll
-                for (int j = 0; j < V; j++) bitsw |= (uint64_t)code[j] << (6 * j);
-                uint8_t* dst = row + c0 * 3 / 4;
-                if (V == 8) {
-                    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
-                    d16[0] = (uint16_t)bitsw; d16[1] = (uint16_t)(bitsw >> 16); d16[2] = (uint16_t)(bitsw >> 32);
-                } else {
-                    dst[0] = (uint8_t)bitsw; dst[1] = (uint8_t)(bitsw >> 8); dst[2] = (uint8_t)(bitsw >> 16);
-                }
+                dst[0] = (uint8_t)bw; dst[1] = (uint8_t)(bw >> 8); dst[2] = (uint8_t)(bw >> 16);
             }
-            if (p.dq) {
-                if (p.dq_bf16) {
-                    uint16_t* dst = static_cast<uint16_t*>(p.dq) + r * p.cols + c0;
+        } else {
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-                    for (int j = 0; j < V; j++) dst[j] = bf16_rne(d[j]);
-                } else {
-                    float* dst = static_cast<float*>(p.dq) + r * p.cols + c0;
+            for (int j = 0; j < 4; j++) lo |= (uint32_t)(code[j] & 0xff) << (8 * j);
+            if constexpr (BF) {
 #pragma unroll
-                    for (int j = 0; j < V; j++) dst[j] = d[j];
-                }
+                for (int j = 0; j < 4; j++) hi |= (uint32_t)(code[4 + j] & 0xff) << (8 * j);
+                *reinterpret_cast<uint2*>(crw + c0) = make_uint2(lo, hi);
+            } else {
+                *reinterpret_cast<uint32_t*>(crw + c0) = lo;
+            }
+        }
+        if (p.dq) {
+            if (p.dq_bf16) {
+                uint16_t* dst = static_cast<uint16_t*>(p.dq) + r * p.cols + c0;
+                uint32_t pk[EPC / 2];
+#pragma unroll
+                for (int j = 0; j < EPC / 2; j++) pk[j] = bf16_rne(d[2 * j]) | ((uint32_t)bf16_rne(d[2 * j + 1]) << 16);
+                if constexpr (BF) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+            } else {
+                float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.dq) + r * p.cols + c0);
+                dst[0] = make_float4(d[0], d[1], d[2], d[3]);
+                if constexpr (BF) dst[1] = make_float4(d[4], d[5], d[6], d[7]);
             }
         }
     }
+    __syncthreads();
 
-    // scales (and offsets): column blocks: V bytes per band row; 2D: one per block
-    if (two_d) {
-        int az = allzero[0];
-#pragma unroll
-        for (int j = 1; j < V; j++) az &= allzero[j];
-        az = group_and_rt(az, G);
-        if (active && leader) {
-            const int64_t sidx = band * (p.cols / BR) + c0 / BR;
-            p.scales[sidx] = (uint8_t)sc[0];
-            if (p.asym) p.offsets[sidx] = kind[0] == 3 ? (uint16_t)0 : ob[0];
-            zb += (unsigned long long)az;
-        }
-    } else if (active) {
-#pragma unroll
-        for (int j = 0; j < V; j++) {
-            const int64_t sidx = band * p.cols + c0 + j;
-            p.scales[sidx] = (uint8_t)sc[j];
-            if (p.asym) p.offsets[sidx] = kind[j] == 3 ? (uint16_t)0 : ob[j];
-            zb += (unsigned long long)allzero[j];
+    // ---- all-zero blocks -------------------------------------------------------
+    {
+        const int col = tid * CPT;
+        const uint32_t full = (1u << CPT) - 1u;
+        const uint32_t bits = (zmask[col >> 5] >> (col & 31)) & full;
+        if (two_d) {
+            // the G1 lanes of a block hold its columns: all of their bits set
+            const int allz = group_and<G1>(bits == full ? 1 : 0);
+            if (col < ncol && tid % G1 == 0) zb += (unsigned long long)allz;
+        } else if (col < ncol) {
+            zb += (unsigned long long)__builtin_popcount(bits);
         }
     }
     if (p.parts) block_stats<NT>(s2, e2, nz, fl, zb, p.parts + blockIdx.x);
 }
 
+constexpr int64_t tile_cols(int in_bf16) { return in_bf16 ? TROW / 2 : TROW / 4; }
+
 }  // namespace
 
 int64_t tiles_grid(const QParams& p) {
-    const int V = p.in_bf16 ? 8 : 4;
-    return ((p.rows / p.br) * (p.cols / V) + NT - 1) / NT;
+    const int64_t tc = tile_cols(p.in_bf16);
+    return (p.rows / p.br) * ((p.cols + tc - 1) / tc);
 }
 
 hipError_t launch_tiles(const QParams& p, hipStream_t s) {

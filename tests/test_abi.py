@@ -85,7 +85,10 @@ def _rows_grid(rows, cols):
 
 
 def _tiles_grid(rows, cols, br, in_bf16):
-    return -(-(rows // br) * (cols // (8 if in_bf16 else 4)) // 256)
+    """workgroups of the column / 2D kernel: one per band of br rows and 1 KiB
+    of each row (512 bf16 or 256 fp32 columns)"""
+    tc = 512 if in_bf16 else 256
+    return (rows // br) * -(-cols // tc)
 
 
 @pytest.mark.parametrize("rows,cols,kw", [

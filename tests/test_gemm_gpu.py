@@ -199,6 +199,110 @@ def test_fp6_quantized_operands(ea, eb):
     assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref) + slack
 
 
+# ---- MXFP8 operands and 8-bit x 6-/4-bit pairs -------------------------------
+# The MX family's 8-bit elements ("Unveiling ... MXFP4", current state: MX
+# formats of 8, 6 and 4 bits; the proposed methods also apply to MXFP8) on the
+# same scaled matrix instruction, type fields 0 (E4M3) and 1 (E5M2).
+FP8 = {"e4m3": oracle.FP8_E4M3, "e5m2": oracle.FP8_E5M2}
+ALL8 = {**{k: v[0] for k, v in ELEMS.items()}, **FP8}
+FP8_PAIRS = [(a, b) for a in ALL8 for b in ALL8 if a in FP8 or b in FP8]
+
+
+def fp8_codes(rng, elem, rows, cols, lo_exp=None):
+    """random FP8 codes without the Inf / NaN encodings; with lo_exp, only
+    magnitudes in [1, 4) (exponent fields lo_exp and lo_exp + 1)"""
+    mb = 3 if elem == oracle.FP8_E4M3 else 2
+    if lo_exp is None:
+        top = 0x7F if elem == oracle.FP8_E4M3 else 0x7C
+        mag = rng.integers(0, top, (rows, cols))
+    else:
+        mag = rng.integers(lo_exp << mb, (lo_exp + 2) << mb, (rows, cols))
+    return (mag | (rng.integers(0, 2, (rows, cols)) << 7)).astype(np.uint8)
+
+
+def codes8(rng, name, rows, cols, narrow):
+    e = ALL8[name]
+    if name in FP8:
+        return fp8_codes(rng, e, rows, cols, (7 if name == "e4m3" else 15) if narrow else None)
+    return rand_codes(rng, e, rows, cols)
+
+
+def fmt8(name):
+    return mx.Format(elem=ALL8[name]), oracle.Format(elem=ALL8[name])
+
+
+@pytest.mark.parametrize("ea,eb", FP8_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(130, 260, 1024), (33, 65, 96)])
+def test_fp8_exact_case(ea, eb, M, N, K):
+    """Unit scales and FP8 magnitudes in [1, 4): every product lies within the
+    instruction's 14-bit summation window of the largest (at most 28 * 4 =
+    112 against a smallest step of 2^-7) and every partial sum is an exact
+    fp32 value (below 2^24 of the smallest step), so fp32 output is bit-exact
+    and bf16 output is the nearest-even rounding of the exact sum.  K = 1024
+    takes the LDS-staged kernel, K = 96 the register-only one."""
+    fa, ra = fmt8(ea)
+    fb, rb = fmt8(eb)
+    rng = np.random.default_rng(M * 3 + N + K)
+    ca, cb = codes8(rng, ea, M, K, True), codes8(rng, eb, N, K, True)
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    da = oracle.dequantize(ra, {"codes": ca, "scales": sa}, M, K)
+    db = oracle.dequantize(rb, {"codes": cb, "scales": sb}, N, K)
+    exact = oracle.gemm_f64(da, db)
+    qa, qb = make_q(ca, sa, M, K), make_q(cb, sb, N, K)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(c32, exact.astype(np.float32))
+    assert np.array_equal(c16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_of(exact))
+
+
+@pytest.mark.parametrize("ea,eb", FP8_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(257, 130, 1024), (64, 96, 352)])
+def test_fp8_random_scales(ea, eb, M, N, K):
+    """Every finite code and random scales: fp32 output within the fp32
+    accumulation bound widened by what the 14-bit summation window may drop
+    (FP8 products span up to 36 binades), bf16 output within 1e-3."""
+    fa, ra = fmt8(ea)
+    fb, rb = fmt8(eb)
+    rng = np.random.default_rng(K + 5)
+    ca, cb = codes8(rng, ea, M, K, False), codes8(rng, eb, N, K, False)
+    sa = rng.integers(118, 137, (M, K // 32), dtype=np.uint8)
+    sb = rng.integers(118, 137, (N, K // 32), dtype=np.uint8)
+    da = oracle.dequantize(ra, {"codes": ca, "scales": sa}, M, K)
+    db = oracle.dequantize(rb, {"codes": cb, "scales": sb}, N, K)
+    ref = oracle.gemm_f64(da, db)
+    qa, qb = make_q(ca, sa, M, K), make_q(cb, sb, N, K)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb).view(torch.int16).cpu().numpy().view(np.uint16)
+    slack = np.linalg.norm(window_bound(da, db))
+    assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref) + slack
+    assert rel_frob(oracle.bf16_bits_to_f32(c16), oracle.bf16_bits_to_f32(bf16_of(ref))) <= 1e-3
+
+
+@pytest.mark.parametrize("ea,eb", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e2m1"), ("e2m1", "e4m3"),
+                                   ("e4m3", "e2m3"), ("e2m3", "e5m2")])
+def test_fp8_quantized_operands(ea, eb):
+    """MXFP8 operands quantized on the GPU, alone and against 6- and 4-bit
+    ones; the product against the oracle's dequantized product, and (soft
+    check) an error against the exact bf16 product well below MXFP4's."""
+    a, b = synth.w5(m=192, n=320, k=1024)
+    fa, ra = fmt8(ea)
+    fb, rb = fmt8(eb)
+    qa, _, _ = mx.mx_quantize(fa, to_dev(a))
+    qb, _, _ = mx.mx_quantize(fb, to_dev(b))
+    da, db = oracle.quantize(a, ra)["dequant"], oracle.quantize(b, rb)["dequant"]
+    ref = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    slack = np.linalg.norm(window_bound(da, db))
+    assert np.linalg.norm(c32 - ref) <= 1e-5 * np.linalg.norm(ref) + slack
+    if ea in FP8 and eb in FP8:
+        exact = synth.bf16_bits_to_f32(a).astype(np.float64) @ synth.bf16_bits_to_f32(b).astype(np.float64).T
+        q4 = oracle.gemm_f64(oracle.quantize(a, oracle.Format())["dequant"], oracle.quantize(b, oracle.Format())["dequant"])
+        err8, err4 = np.linalg.norm(c32 - exact), np.linalg.norm(q4 - exact)
+        assert err8 < err4 / 1.5         # E4M3 about 3.9x lower, E5M2 about 2x
+
+
 # ---- macro-block scaled MXFP4 ("Unveiling ... MXFP4", Sec. 4, MBS, Fig. 5) -----
 MBS_ORACLE = oracle.Format(macro_cols=128)
 MBS_DEV = mx.Format(macro_cols=128)

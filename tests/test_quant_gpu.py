@@ -13,7 +13,7 @@ from parity import check_dequantize, check_quantize
 
 pytestmark = pytest.mark.gpu
 
-E2M1, INT4, E2M3, E3M2, E3M0 = 0, 1, 2, 3, 4
+E2M1, INT4, E2M3, E3M2, E3M0, E4M3, E5M2 = 0, 1, 2, 3, 4, 5, 6
 E8M0, UE4M3, NVFP4, UE5M3, SE3M0 = 0, 1, 2, 3, 4
 FLOOR, CEIL, OAS = 0, 1, 2
 RTNE, SR, CEILR = 0, 1, 2
@@ -88,7 +88,10 @@ ELEM_FORMATS = [dict(elem=INT4), dict(elem=INT4, rule=CEIL), dict(elem=E2M3), di
                 dict(asymmetric=1), dict(asymmetric=1, rule=CEIL, round=SR, seed=1),
                 dict(elem=INT4, asymmetric=1, rule=OAS, oas_tau=20.0),
                 dict(scale=UE5M3, elem=E3M2, block_cols=16), dict(scale=NVFP4, elem=INT4, block_cols=16),
-                dict(scale=SE3M0, rule=CEIL, elem=E2M3)]
+                dict(scale=SE3M0, rule=CEIL, elem=E2M3),
+                dict(elem=E4M3), dict(elem=E5M2, rule=CEIL), dict(elem=E4M3, round=SR, seed=13),
+                dict(elem=E5M2, round=CEILR), dict(elem=E4M3, rule=OAS, oas_tau=500.0),
+                dict(elem=E5M2, scale=UE5M3, block_cols=16)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -121,7 +124,8 @@ def test_fast_kernel_instantiations(dtype, b, rule):
 
 # ---- column and 2D blocks of every size, both dtypes
 TILE_FORMATS = [dict(), dict(round=SR, seed=3), dict(scale=NVFP4), dict(elem=INT4, asymmetric=1, rule=CEIL),
-                dict(asymmetric=1), dict(elem=E3M2), dict(scale=UE5M3, rule=CEIL), dict(scale=SE3M0, rule=CEIL)]
+                dict(asymmetric=1), dict(elem=E3M2), dict(scale=UE5M3, rule=CEIL), dict(scale=SE3M0, rule=CEIL),
+                dict(elem=E4M3), dict(elem=E5M2, round=SR, seed=4)]
 
 
 @pytest.mark.parametrize("b", [8, 16, 32])
@@ -183,7 +187,8 @@ def test_special_values():
     for kw in (dict(), dict(rule=CEIL), dict(rule=OAS, oas_tau=7.5), dict(scale=NVFP4, block_cols=16),
                dict(scale=UE5M3, block_cols=16), dict(scale=UE4M3, block_cols=16), dict(round=SR, seed=11),
                dict(elem=INT4, asymmetric=1, rule=CEIL), dict(asymmetric=1), dict(scale=SE3M0, rule=CEIL),
-               dict(elem=E3M2), dict(round=CEILR), dict(block_rows=8, block_cols=8)):
+               dict(elem=E3M2), dict(round=CEILR), dict(block_rows=8, block_cols=8), dict(elem=E4M3),
+               dict(elem=E5M2, block_rows=8, block_cols=1), dict(asymmetric=1, block_rows=8, block_cols=8)):
         check_quantize(x, kw, f"special {kid(kw)}")
 
 
