@@ -19,7 +19,18 @@ __global__ __launch_bounds__(NT) void k_tensor_scale(const float* parts, int64_t
                                                      float* ts, int32_t* re) {
     __shared__ float sh[NT / 64];
     float a = 0.f;
-    for (int64_t i = threadIdx.x; i < n; i += NT) a = fmaxf(a, parts[i]);
+    // eight independent loads in flight per thread
+    constexpr int U = 8;
+    for (int64_t base = threadIdx.x; base < n; base += (int64_t)NT * U) {
+        float q[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t i = base + (int64_t)u * NT;
+            q[u] = i < n ? parts[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) a = fmaxf(a, q[u]);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = a;

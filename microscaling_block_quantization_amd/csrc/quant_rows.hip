@@ -166,6 +166,8 @@ __device__ __forceinline__ float block_max(float a) {
     return m;
 }
 
+typedef float f2vr __attribute__((ext_vector_type(2)));
+
 // CH elements per thread, W = min(block_cols, CH) elements per block in a thread
 template <bool BF, int CH, int W>
 __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
@@ -301,6 +303,40 @@ __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
 
         const float down = pow2f(-e), up = pow2f(e);
         int allzero = 1;
+        if (E.kind == E2M1 && p.round == RTNE && kind != 3) {
+            // E2M1 to nearest: two elements per hardware convert (RTNE with
+            // saturation, signed zero kept) and two per decode; a power-of-two
+            // scale decodes as q * 2^e exactly (the convert reads the scale's
+            // exponent field; 2^-127 is the zero field)
+#pragma unroll
+            for (int i = 0; i < W; i += 2) {
+                const int k = j * W + i;
+                float v[2];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const float yk = y[k + h];
+                    if (kind == 0) v[h] = (p.asym ? (yk - o) : yk) * down;
+                    else if (kind == 1) v[h] = yk / S;
+                    else v[h] = (fbits(yk) >> 31) ? -0.f : 0.f;
+                }
+                const uint32_t cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+                const f2vr q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, kind == 0 ? up : 1.0f, 0);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    float dv = q[h];
+                    if (kind == 0) {
+                        if (p.asym) dv = dv + o;
+                        if (p.macro_cols) dv = dv * sM;
+                    } else {
+                        dv = dv * sb;
+                        if (p.scale == SC_NVFP4) dv = dv * g;
+                    }
+                    code[k + h] = (int)((cw >> (4 * h)) & 0xfu);
+                    d[k + h] = dv;
+                    allzero &= (dv == 0.f);
+                }
+            }
+        } else
 #pragma unroll
         for (int i = 0; i < W; i++) {
             const int k = j * W + i;
@@ -343,16 +379,30 @@ __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
         if (p.dq) store_dq<CH>(p, r, c0, d);
     }
     if (p.parts) {
+        // the thread's sums in fp32, then float64 (the whole thread in float64
+        // when a square leaves the fp32 range, or a NaN is present)
         double s2 = 0, e2 = 0;
         unsigned long long nz = 0, fl = 0;
         if (active) {
+            float s2f = 0.f, e2f = 0.f;
 #pragma unroll
             for (int i = 0; i < CH; i++) {
-                double xv = x[i], dv = d[i];
-                s2 += xv * xv;
-                e2 += (xv - dv) * (xv - dv);
+                const float ri = x[i] - d[i];
+                s2f = __builtin_fmaf(x[i], x[i], s2f);
+                e2f = __builtin_fmaf(ri, ri, e2f);
                 nz += (x[i] != 0.f);
                 fl += (x[i] != 0.f && d[i] == 0.f);
+            }
+            if (fabsf(s2f) < INFINITY && fabsf(e2f) < INFINITY) {
+                s2 = s2f;
+                e2 = e2f;
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; i++) {
+                    const double xv = x[i], dv = d[i];
+                    s2 += xv * xv;
+                    e2 += (xv - dv) * (xv - dv);
+                }
             }
         }
         block_stats<NT>(s2, e2, nz, fl, zb, p.parts + blockIdx.x);
