@@ -38,12 +38,18 @@ hipError_t launch_rows(const QParams& p, bool amax_only, hipStream_t s);
 bool rows_fast_ok(const QParams& p);
 int64_t rows_fast_grid(const QParams& p);   // upper bound of the grid launch_rows_fast uses
 hipError_t launch_rows_fast(const QParams& p, hipStream_t s, int64_t* grid);
+// the other E2M1 round-to-nearest row formats on the hardware FP4 converter
+// (fp8 block scales, block Hadamard rotation, macro-block scales)
+bool rows_hw_ok(const QParams& p);
+int64_t rows_hw_grid(const QParams& p);     // upper bound of the grid launch_rows_hw uses
+hipError_t launch_rows_hw(const QParams& p, hipStream_t s, int64_t* grid);
 // column (b x 1) and 2D (b x b) blocks
 int64_t tiles_grid(const QParams& p);
 hipError_t launch_tiles(const QParams& p, hipStream_t s);
-// plain tensor abs-max pre-pass (no rotation)
+// tensor abs-max pre-pass (after the rotation, if any): amax_grid bounds the
+// number of per-workgroup maxima; launch_amax reports the number written
 int64_t amax_grid(const QParams& p);
-hipError_t launch_amax(const QParams& p, hipStream_t s);
+hipError_t launch_amax(const QParams& p, hipStream_t s, int64_t* grid);
 // finalize: tensor scale / reference exponent from the per-workgroup maxima
 hipError_t launch_tensor_scale(const float* parts, int64_t n, int scale_kind, float qmax,
                                float* tensor_scale, int32_t* ref_exp, hipStream_t s);

@@ -715,6 +715,266 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
     if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, p.parts + blockIdx.x);
 }
 
+// ---------------------------------------------------------------------------
+// Hardware-convert row kernel for the other E2M1 round-to-nearest formats:
+// UE4M3 / UE5M3 / NVFP4 block scales, block Hadamard rotation ("Bridging the
+// Gap ... Microscaling FP4 Quantization", Sec. 2.2) and macro-block scaling
+// ("Unveiling the Potential of Quantization with MXFP4", Sec. 4), with E8M0
+// or fp8 block scales; dense rows, no dequantized output.  Wave tile, buffer
+// I/O and grid-stride loop as in k_rows_fast; the lane groups (scale block: g
+// lanes, rotation chunk: hg, macro block: mg) are uniform run-time sizes.
+//  - rotation: the butterflies of a chunk's EPC elements in registers, then
+//    one stage per lane bit with the partner lane's value (DPP for lane
+//    distances 1 and 2, ds_swizzle beyond), in the definition's stage order;
+//    the upper lane of a pair forms partner - own as fma(own, -1, partner),
+//    which is the same single rounding; then times the fp32 1/sqrt(h);
+//  - macro scale: the finite maximum over mg lanes, s_M = UE4M3 rounding of
+//    the significand of M / 6; the elements are divided by s_M;
+//  - E8M0 scales: the scaled FP4 convert divides by the power of two itself
+//    (it reads the exponent field of the scale operand); fp8 scales: the
+//    elements are divided by S (correctly rounded) and converted unscaled;
+//  - decode by the matching FP4 -> f32 convert, times s_b (and g) or s_M.
+// ---------------------------------------------------------------------------
+struct HwArgs {
+    int64_t nchunks;
+    int g, hg, mg;           // lanes per scale block, rotation chunk, macro block (0: none)
+    int floor_rule;          // E8M0: FLOOR, else the smallest e with q 2^e >= amax
+    int lq;                  // q = 2^lq (1 + fq 2^-23): 6 (CEIL) or tau (OAS)
+    uint32_t fq;
+    int ue5, nvfp4;          // fp8 scales: UE5M3, NVFP4 (UE4M3 times the tensor scale)
+    float hconst;            // fp32 rounding of 1 / sqrt(h)
+};
+
+// the value of lane l ^ S of the wave (S a power of two below 32)
+template <int S>
+__device__ __forceinline__ float xlane(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (S == 1) return __uint_as_float(dpp<DPP_XOR1>(u));
+    else if constexpr (S == 2) return __uint_as_float(dpp<DPP_XOR2>(u));
+    else return __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x1f | (S << 10)));
+}
+
+// NP pairs of fp32 values to E2M1 codes (pair i in byte i): the scaled convert
+// (round to nearest even, saturating, divided by the power of two whose
+// exponent field `scale` carries); and the codes back to values times it
+template <int NP>
+__device__ __forceinline__ uint32_t enc_fp4(const float* v, float scale) {
+    uint32_t cw = 0;
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[0], v[1], scale, 0);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[2], v[3], scale, 1);
+    if constexpr (NP == 4) {
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[4], v[5], scale, 2);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[6], v[7], scale, 3);
+    }
+    return cw;
+}
+template <int NP>
+__device__ __forceinline__ void dec_fp4(uint32_t cw, float scale, float* d) {
+    f2v q[NP];
+    q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 0);
+    q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 1);
+    if constexpr (NP == 4) {
+        q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 2);
+        q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 3);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; i++) { d[2 * i] = q[i][0]; d[2 * i + 1] = q[i][1]; }
+}
+
+// one rotation stage across lanes at distance S: lower lane a + b, upper a - b
+template <int S, int EPC>
+__device__ __forceinline__ void had_stage(float (&x)[EPC], int lane) {
+    const float sg = (lane & S) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < EPC; i++) x[i] = __builtin_fmaf(x[i], sg, xlane<S>(x[i]));
+}
+
+// maximum over aligned groups of g lanes (g uniform, a power of two <= 64)
+__device__ __forceinline__ uint32_t group_max_g(uint32_t v, int g) {
+    if (g >= 2) v = max(v, dpp<DPP_XOR1>(v));
+    if (g >= 4) v = max(v, dpp<DPP_XOR2>(v));
+    if (g >= 8) v = max(v, dpp<DPP_HALF_MIRROR>(v));
+    if (g >= 16) v = max(v, dpp<DPP_ROW_MIRROR>(v));
+    if (g >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+    if (g >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+    return v;
+}
+
+// AMAX: the tensor pre-pass of NVFP4 scales instead: the finite maximum of
+// |x| (after the rotation) per workgroup into p.amax_parts
+template <bool BF, bool FP8S, bool ST, bool AMAX = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
+    constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
+    constexpr int CB = EPC / 2;            // code bytes per chunk
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (h.nchunks + TILE_CH - 1) / TILE_CH;
+    const int64_t step = (int64_t)gridDim.x * (NT / 64);
+    const char* xin = static_cast<const char*>(p.x);
+    const int lin = lane * 16, lco = lane * CB;
+    const bool lead = lane % h.g == 0;
+    const int lsc = lead ? lane / h.g : OOB_OFFSET;
+    const int lmc = (h.mg && lane % h.mg == 0) ? lane / h.mg : OOB_OFFSET;
+    const float gts = (FP8S && h.nvfp4 && !AMAX) ? *p.tensor_scale : 1.0f;
+    uint32_t tmax = 0;                     // AMAX: finite maximum of |x| as float bits
+    double s2d = 0.0, e2d = 0.0;
+    uint32_t nz = 0, fl = 0, zb = 0;
+
+    auto valid = [&](int64_t t) -> int {
+        const int64_t r = h.nchunks - t * TILE_CH;
+        return r <= 0 ? 0 : (r < TILE_CH ? (int)r : TILE_CH);
+    };
+    for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < ntiles; t += step) {
+        const int nv = valid(t);
+        const rsrc_t rx = buf(xin + t * TILE_CH * 16, nv * 16);
+        const rsrc_t rc = buf(p.codes + t * TILE_CH * CB, nv * CB);
+        const rsrc_t rs = buf(p.scales + t * (TILE_CH / h.g), nv / h.g);
+        const rsrc_t rm = buf(h.mg ? p.macro + t * (TILE_CH / (h.mg ? h.mg : 1)) : p.codes, h.mg ? nv / h.mg : 0);
+        u32x4 w[FAST_NL];
+#pragma unroll
+        for (int k = 0; k < FAST_NL; k++)
+            w[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lin + k * 1024, 0, CPOL_NT));
+#pragma unroll
+        for (int k = 0; k < FAST_NL; k++) {
+            float x[EPC];
+#pragma unroll
+            for (int i = 0; i < EPC; i++)
+                x[i] = BF ? ((i & 1) ? bf16hi(w[k][i >> 1]) : bf16lo(w[k][i >> 1])) : __uint_as_float(w[k][i]);
+            if (h.hg) {
+#pragma unroll
+                for (int span = 1; span < EPC; span <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        if (i & span) continue;
+                        const float a = x[i], b = x[i + span];
+                        x[i] = a + b;
+                        x[i + span] = a - b;
+                    }
+                }
+                if (h.hg > 1) had_stage<1>(x, lane);
+                if (h.hg > 2) had_stage<2>(x, lane);
+                if (h.hg > 4) had_stage<4>(x, lane);
+                if (h.hg > 8) had_stage<8>(x, lane);
+                if (h.hg > 16) had_stage<16>(x, lane);
+#pragma unroll
+                for (int i = 0; i < EPC; i++) x[i] = x[i] * h.hconst;
+            }
+            if constexpr (AMAX) {
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    const uint32_t u = __float_as_uint(x[i]) & 0x7fffffffu;
+                    if (u < 0x7f800000u) tmax = max(tmax, u);
+                }
+                continue;
+            }
+            // macro-block scale over mg lanes
+            float y[EPC];
+            float sM = 1.0f;
+            uint32_t smc = 0x38u;
+            if (h.mg) {
+                uint32_t mb = 0;
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    const uint32_t u = __float_as_uint(x[i]) & 0x7fffffffu;
+                    if (u < 0x7f800000u) mb = max(mb, u);
+                }
+                mb = group_max_g(mb, h.mg);
+                if (mb) {
+                    const float tt = __uint_as_float(mb) / 6.0f;
+                    const float mu = tt * pow2f(-flog2(tt));
+                    smc = (uint32_t)fp8_code(false, mu);
+                    sM = fp8_value(false, (int)smc);
+                }
+#pragma unroll
+                for (int i = 0; i < EPC; i++) y[i] = x[i] / sM;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)smc, rm, lmc + k * (64 / h.mg), 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPC; i++) y[i] = x[i];
+            }
+            // the block maximum: float bits of |y|; NaN and Inf sort above every finite value
+            uint32_t am = 0;
+#pragma unroll
+            for (int i = 0; i < EPC; i++) am = max(am, __float_as_uint(y[i]) & 0x7fffffffu);
+            am = group_max_g(am, h.g);
+            const bool nonfinite = am >= 0x7f800000u;
+            uint32_t cw = 0, code;
+            float d[EPC];
+            if constexpr (!FP8S) {
+                uint32_t sbits;
+                if (h.floor_rule) sbits = __builtin_elementwise_sub_sat(am & 0x7f800000u, 0x01000000u);
+                else sbits = (uint32_t)(fast_exp<false>(am, h.lq, h.fq) + 127) << 23;
+                code = sbits >> 23;
+                const float scale = __uint_as_float(sbits);
+                cw = enc_fp4<EPC / 2>(y, scale);
+                if (nonfinite) cw = 0;
+                dec_fp4<EPC / 2>(cw, scale, d);
+#pragma unroll
+                for (int i = 0; i < EPC; i++) d[i] = d[i] * sM;
+                if (nonfinite) code = 0xffu;
+            } else {
+                float tt = __uint_as_float(am) / 6.0f;
+                if (h.nvfp4) tt = tt / gts;
+                const int sc = fp8_code(h.ue5 != 0, tt);
+                const float sb = fp8_value(h.ue5 != 0, sc);
+                const float S = h.nvfp4 ? sb * gts : sb;
+                float v[EPC];
+#pragma unroll
+                for (int i = 0; i < EPC; i++) v[i] = S == 0.f ? ((__float_as_uint(y[i]) >> 31) ? -0.f : 0.f) : y[i] / S;
+                cw = enc_fp4<EPC / 2>(v, 1.0f);
+                if (nonfinite) cw = 0;
+                dec_fp4<EPC / 2>(cw, 1.0f, d);
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    d[i] = d[i] * sb;
+                    if (h.nvfp4) d[i] = d[i] * gts;
+                }
+                code = nonfinite ? (h.ue5 ? 0xffu : 0x7fu) : (uint32_t)sc;
+            }
+            if (nonfinite) {
+#pragma unroll
+                for (int i = 0; i < EPC; i++) d[i] = __uint_as_float(0x7fc00000u);
+            }
+            if constexpr (BF) __builtin_amdgcn_raw_buffer_store_b32(cw, rc, lco + k * 64 * CB, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)cw, rc, lco + k * 64 * CB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs, lsc + k * (64 / h.g), 0, 0);
+            if constexpr (ST) {
+                float s2c = 0.f, e2c = 0.f;
+                uint32_t nzl = 0;
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    const float ri = x[i] - d[i];
+                    s2c = __builtin_fmaf(x[i], x[i], s2c);
+                    e2c = __builtin_fmaf(ri, ri, e2c);
+                    nz += (x[i] != 0.f);
+                    fl += (x[i] != 0.f && d[i] == 0.f);
+                    nzl |= (d[i] != 0.f) ? 1u : 0u;    // NaN counts as non-zero
+                }
+                if (fabsf(s2c) < INFINITY && fabsf(e2c) < INFINITY) {
+                    s2d += (double)s2c;
+                    e2d += (double)e2c;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        const double xd = x[i], dd = d[i];
+                        s2d += xd * xd;
+                        e2d += (xd - dd) * (xd - dd);
+                    }
+                }
+                nzl = group_max_g(nzl, h.g);
+                zb += (lead && nzl == 0 && lane + k * 64 < nv) ? 1u : 0u;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (AMAX) {
+        const float a = block_max<NT>(__uint_as_float(tmax));
+        if (threadIdx.x == 0) p.amax_parts[blockIdx.x] = a;
+    } else if constexpr (ST) {
+        block_stats<NT>(s2d, e2d, nz, fl, zb, p.parts + blockIdx.x);
+    }
+}
+
 int fast_g(const QParams& p) { return p.bc / (p.in_bf16 ? 8 : 4); }
 
 int64_t fast_groups(const QParams& p) {
@@ -794,6 +1054,83 @@ hipError_t launch_rows_fast(const QParams& p, hipStream_t s, int64_t* grid) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_amax(const QParams& p, hipStream_t s) { return launch_rows(p, true, s); }
+namespace {
+template <bool BF, bool FP8S>
+hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
+    const bool st = p.parts != nullptr;
+    auto k = st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>;
+    static int64_t cache[2] = {0, 0};   // one per statistics variant
+    int64_t g = fast_groups(p);
+    const int64_t r = resident(k, &cache[st ? 1 : 0]);
+    if (g > r) g = r;
+    if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
+    *grid = g;
+    if (g == 0) return hipSuccess;
+    k<<<g, NT, 0, s>>>(p, h);
+    return hipGetLastError();
+}
+}  // namespace
+
+namespace {
+void hw_args(const QParams& p, HwArgs& h) {
+    const int epc = p.in_bf16 ? 8 : 4;
+    h.nchunks = p.rows * p.cols / epc;
+    h.g = p.bc / epc;
+    h.hg = p.had ? p.had / epc : 0;
+    h.mg = p.macro_cols ? 128 / epc : 0;
+    h.floor_rule = p.rule == RULE_FLOOR;
+    const float q = p.rule == RULE_OAS ? p.tau : 6.0f;
+    uint32_t qb;
+    memcpy(&qb, &q, 4);
+    h.lq = (int)(qb >> 23) - 127;
+    h.fq = qb & 0x7fffffu;
+    h.ue5 = p.scale == SC_UE5M3;
+    h.nvfp4 = p.scale == SC_NVFP4;
+    const uint32_t hc = p.had == 16 ? 0x3E800000u : p.had == 32 ? 0x3E3504F3u : p.had == 64 ? 0x3E000000u : 0x3DB504F3u;
+    memcpy(&h.hconst, &hc, 4);
+}
+}  // namespace
+
+bool rows_hw_ok(const QParams& p) {
+    const int epc = p.in_bf16 ? 8 : 4;
+    const bool scale_ok = p.scale == SC_E8M0 || p.scale == SC_UE4M3 || p.scale == SC_UE5M3 || p.scale == SC_NVFP4;
+    const int g = p.bc / epc;
+    return p.elem == E2M1 && p.round == RTNE && !p.asym && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
+           g >= 1 && g <= 64 && g * epc == p.bc && (!p.had || p.had >= epc) && (!p.macro_cols || p.scale == SC_E8M0);
+}
+
+int64_t rows_hw_grid(const QParams& p) { return rows_fast_grid(p); }
+
+hipError_t launch_rows_hw(const QParams& p, hipStream_t s, int64_t* grid) {
+    *grid = 0;
+    HwArgs h;
+    hw_args(p, h);
+    const bool fp8s = p.scale != SC_E8M0;
+    if (p.in_bf16) return fp8s ? launch_hw_t<true, true>(p, h, s, grid) : launch_hw_t<true, false>(p, h, s, grid);
+    return fp8s ? launch_hw_t<false, true>(p, h, s, grid) : launch_hw_t<false, false>(p, h, s, grid);
+}
+
+// The NVFP4 / E3M0 tensor pre-pass: on the wave-tile kernel (dense rows of a
+// format it takes), else on the general row kernel.  *grid: the partials written.
+hipError_t launch_amax(const QParams& p, hipStream_t s, int64_t* grid) {
+    QParams a = p;
+    a.dq = nullptr;
+    if (rows_hw_ok(a)) {
+        HwArgs h;
+        hw_args(a, h);
+        auto k = a.in_bf16 ? k_rows_hw<true, true, false, true> : k_rows_hw<false, true, false, true>;
+        static int64_t cache[2] = {0, 0};
+        int64_t g = fast_groups(a);
+        const int64_t r = resident(k, &cache[a.in_bf16 ? 1 : 0]);
+        if (g > r) g = r;
+        if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
+        *grid = g;
+        if (g == 0) return hipSuccess;
+        k<<<g, NT, 0, s>>>(a, h);
+        return hipGetLastError();
+    }
+    *grid = rows_grid(p);
+    return launch_rows(p, true, s);
+}
 
 }  // namespace mxk
