@@ -362,13 +362,18 @@ def main():
 
     # for information, outside the timed steps: the quantizer alone (codes and
     # scales, no statistics), the form a layer uses when fidelity is not wanted
-    def codes_only():
-        s = codes_only.i % args.sets
-        codes_only.i += 1
+    # (enqueued back to back like the steps, events at the boundaries)
+    reps = 20
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        s = i % args.sets
+        ev2[i][0].record()
         mx.mx_quantize(fmt, A[s], out=qa, workspace=wsa)
         mx.mx_quantize(fmt, B[s], out=qb, workspace=wsb)
-    codes_only.i = 0
-    q0_med, q0 = timed(torch, codes_only, 20)
+        ev2[i][1].record()
+    torch.cuda.synchronize()
+    t0s = [e[0].elapsed_time(e[1]) for e in ev2]
+    q0, q0_med = sum(t0s) / reps, statistics.median(t0s)
     # the step left A's and B's codes of the last input set; recompute them (and
     # the product) for the fidelity figures and the parity check below
     s_last = (args.steps - 1) % args.sets

@@ -312,20 +312,43 @@ struct StatPart {
     unsigned long long nonzero, flushed, zero_blocks, pad;
 };
 
+// another lane's value under a DPP control that gives every lane a source
+// (quad permutations, row mirrors): a VALU move, no LDS round trip
+template <int CTRL>
+__device__ __forceinline__ uint32_t lane_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long lane_mov(unsigned long long v) {
+    return ((unsigned long long)lane_mov<CTRL>((uint32_t)(v >> 32)) << 32) | lane_mov<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ double lane_mov(double v) {
+    return __longlong_as_double((long long)lane_mov<CTRL>((unsigned long long)__double_as_longlong(v)));
+}
+
+// Sum over the 64 lanes, the same bits in every lane: pairs (quad_perm
+// [1,0,3,2]), quads ([2,3,0,1]), the two quads of each 8 (half-row mirror),
+// the two halves of each row of 16 (row mirror), then rows 16 and 32 apart.
+// Every step adds two partners' values, which both get the same sum (addition
+// is commutative), so the tree and the result are fixed.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += lane_mov<0xB1>(v);
+    v += lane_mov<0x4E>(v);
+    v += lane_mov<0x141>(v);
+    v += lane_mov<0x140>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
     return v;
 }
 
-// block-wide sum of one StatPart per thread; thread 0 writes it to dst
-// Workgroup sums of the per-thread statistics, valid in thread 0.  Wave
-// butterflies then the waves in index order: the result does not depend on
-// timing.
-template <int NT>
-__device__ __forceinline__ StatPart block_sum(double s2, double e2, unsigned long long nz,
-                                              unsigned long long fl, unsigned long long zb) {
+// Workgroup sums of the per-thread statistics, valid in thread 0.  Wave sums,
+// then the waves in index order: the result does not depend on timing.  C is
+// the type the per-thread counts are summed in within a wave (32 bits where a
+// workgroup's counts are known to fit).
+template <int NT, typename C = unsigned long long>
+__device__ __forceinline__ StatPart block_sum(double s2, double e2, C nz, C fl, C zb) {
     __shared__ double sh_d[2][NT / 64];
     __shared__ unsigned long long sh_u[3][NT / 64];
     s2 = wave_sum(s2);
@@ -350,11 +373,9 @@ __device__ __forceinline__ StatPart block_sum(double s2, double e2, unsigned lon
     return p;
 }
 
-template <int NT>
-__device__ __forceinline__ void block_stats(double s2, double e2, unsigned long long nz,
-                                            unsigned long long fl, unsigned long long zb,
-                                            StatPart* dst) {
-    const StatPart p = block_sum<NT>(s2, e2, nz, fl, zb);
+template <int NT, typename C = unsigned long long>
+__device__ __forceinline__ void block_stats(double s2, double e2, C nz, C fl, C zb, StatPart* dst) {
+    const StatPart p = block_sum<NT, C>(s2, e2, nz, fl, zb);
     if (threadIdx.x == 0) *dst = p;
 }
 
