@@ -311,6 +311,7 @@ struct StatPart {
     double sig2, err2;
     unsigned long long nonzero, flushed, zero_blocks, pad;
 };
+static_assert(sizeof(StatPart) == 48, "a statistics partial is three 16-byte words");
 
 // another lane's value under a DPP control that gives every lane a source
 // (quad permutations, row mirrors): a VALU move, no LDS round trip
@@ -327,19 +328,52 @@ __device__ __forceinline__ double lane_mov(double v) {
     return __longlong_as_double((long long)lane_mov<CTRL>((unsigned long long)__double_as_longlong(v)));
 }
 
+// V_PERMLANE16_SWAP / V_PERMLANE32_SWAP on two copies a, b of a value:
+// afterwards a holds the lower and b the upper partner's value (rows R lanes
+// apart) in every lane
+template <int R>
+__device__ __forceinline__ void swap_rows(uint32_t& a, uint32_t& b) {
+    if constexpr (R == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    }
+}
+// lower + upper partner (R lanes apart), the same bits in both lanes
+template <int R, typename T>
+__device__ __forceinline__ T row_pair_sum(T v) {
+    if constexpr (sizeof(T) == 4) {
+        uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+        swap_rows<R>(a, b);
+        return __builtin_bit_cast(T, a) + __builtin_bit_cast(T, b);
+    } else {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+        uint32_t al = (uint32_t)u, bl = al, ah = (uint32_t)(u >> 32), bh = ah;
+        swap_rows<R>(al, bl);
+        swap_rows<R>(ah, bh);
+        return __builtin_bit_cast(T, ((unsigned long long)ah << 32) | al) +
+               __builtin_bit_cast(T, ((unsigned long long)bh << 32) | bl);
+    }
+}
+
 // Sum over the 64 lanes, the same bits in every lane: pairs (quad_perm
 // [1,0,3,2]), quads ([2,3,0,1]), the two quads of each 8 (half-row mirror),
-// the two halves of each row of 16 (row mirror), then rows 16 and 32 apart.
-// Every step adds two partners' values, which both get the same sum (addition
-// is commutative), so the tree and the result are fixed.
+// the two halves of each row of 16 (row mirror), then rows 16 and 32 apart
+// (row swaps).  Every step adds two partners' values, which both get the
+// same sum (addition is commutative), so the tree and the result are fixed.
+// All 64 lanes must be active.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
     v += lane_mov<0xB1>(v);
     v += lane_mov<0x4E>(v);
     v += lane_mov<0x141>(v);
     v += lane_mov<0x140>(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    v = row_pair_sum<16>(v);
+    v = row_pair_sum<32>(v);
     return v;
 }
 

@@ -282,3 +282,11 @@ def test_ceilings_library_exports_its_header():
     L = ceilings.lib()
     assert L.mxc_mfma_loop_flops(256, 10) == 2.0 * 32 * 32 * 64 * 16 * 8 * 256 * 10
     assert L.mxc_copy(None, None, 16, None) == 1 and L.mxc_mfma_loop(None, None, 1, 1, None) == 1
+
+
+def test_header_sizes_match_the_binding():
+    """The sizes include/mx.h states are the ones the Python binding uses."""
+    import re
+    src = open(os.path.join(ROOT, "include", "mx.h")).read()
+    defs = {m.group(1): m.group(2) for m in re.finditer(r"#define\s+(MX_\w+)\s+\(?([0-9u<\s]+)\)?", src)}
+    assert eval(defs["MX_NOALLOC_SCRATCH_BYTES"].replace("u", "")) == mx.NOALLOC_SCRATCH_BYTES

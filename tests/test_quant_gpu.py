@@ -311,3 +311,34 @@ def test_strided_input_takes_the_general_kernel(kw):
     for k in ("nonzero", "flushed", "zero_blocks", "n"):
         assert s1[k] == s2[k]
     check_quantize(x, kw, f"dense {kid(kw)}")
+
+
+def test_one_workspace_serves_every_call():
+    """One workspace, large enough for all of them and filled with a stale
+    pattern, serves a run of statistics calls of different formats, shapes
+    and kernel routes (fast rows, hardware-convert rows, general rows, 2D
+    tiles, an empty tensor), each matching the oracle."""
+    import microscaling_block_quantization_amd as mx
+    from parity import compare_stats, to_dev
+    import oracle
+    cases = [(synth.w2(1.0, shape=(256, 1024), seed=11), dict()),
+             (synth.w2(0.02, shape=(128, 2048), seed=12), dict(scale=NVFP4, block_cols=16)),
+             (synth.w2(1.0, shape=(64, 512), seed=13), dict(elem=E2M3, rule=CEIL)),
+             (synth.w2(1.0, shape=(96, 256), seed=14), dict(block_rows=32, block_cols=32)),
+             (synth.w2(1.0, shape=(256, 1024), seed=11), dict()),
+             (np.zeros((0, 64), dtype=np.float32), dict())]
+    need = max(mx.mx_query_sizes(mx.Format(**kw), *x.shape)["workspace"] for x, kw in cases)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    for i, (x, kw) in enumerate(cases):
+        fmt = mx.Format(**kw)
+        xd = to_dev(x) if x.size else torch.empty(x.shape, dtype=torch.float32, device="cuda")
+        q = mx.alloc_qtensor(fmt, *x.shape, xd.device)
+        st = torch.full((64,), 0xA5, dtype=torch.uint8, device=xd.device)
+        mx.mx_quantize(fmt, xd, out=q, stats=st, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.quantize(x, oracle.Format(**kw))
+        got = mx.stats_to_dict(st)
+        if x.size == 0:
+            assert got["n"] == 0 and got["sig2"] == 0 and got["nonzero"] == 0
+        else:
+            compare_stats(ref["stats"], got, f"shared workspace call {i} {kid(kw)}")
