@@ -141,6 +141,21 @@ def ceilings(torch, dev):
             "ms": round(med, 4), "tflops": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4),
             "note": f"{grid} workgroups x 8 waves, 4x2 tiles of the 32x32x64 scaled FP4 instruction fed by "
                     f"ds_read_b128 (6 per 8 instructions), {kind} operand bytes"}
+    # the GEMM's operand stream alone: as many 32 KiB stages per CU as the step's
+    # product moves (7 tiles of 256 x 256 per CU, 32 stages of K = 128 each)
+    tiles_per_cu = -(-((M // 256) * (N // 256)) // grid)
+    stages = tiles_per_cu * (K // 128)
+    src = torch.empty(4 << 20, dtype=torch.uint8, device=dev)
+    src.random_(0, 256)
+    words = torch.empty(grid * 512, dtype=torch.int32, device=dev)
+    cl.lds_dma(src, words, grid, stages)
+    med, _ = timed(torch, lambda: cl.lds_dma(src, words, grid, stages), 10)
+    byt = grid * stages * cl.DMA_STAGE_BYTES
+    out["lds_dma_stream"] = {
+        "ms": round(med, 4), "gbs": round(byt / med / 1e6, 1), "gbs_per_cu": round(byt / grid / med / 1e6, 2),
+        "note": f"{grid} workgroups x {stages} stages of 32 KiB (512 rows x 64 B) into LDS by buffer_load_dwordx4 ... "
+                f"lds, two stages in flight, a barrier per stage: the step's GEMM operand stream without its "
+                f"arithmetic, so its time is a floor for that GEMM on this tiling"}
     return out
 
 
@@ -444,6 +459,8 @@ def main():
         out["roofline"]["frac_of_mfma_loop_random"] = round(
             tfs(g_ms) / ceil["fp4_mfma_loop_random"]["tflops"], 4)
         out["quantize_roofline"]["frac_of_read4_write1"] = round(gbs(q_ms) / ceil["read4_write1"]["gbs"], 4)
+        # the operand stream alone takes this long: the product's time over it
+        out["roofline"]["ms_over_lds_dma_stream"] = round(g_ms / ceil["lds_dma_stream"]["ms"], 3)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -13,7 +13,11 @@
  *    8 waves per workgroup, one workgroup per CU, each wave 4 x 2 tiles of
  *    32 x 32, six 16-byte reads per eight instructions.  Its rate on random
  *    operand bytes is the matrix unit's sustained ceiling under the GPU's
- *    power limit (operands that toggle fewer bits run faster).
+ *    power limit (operands that toggle fewer bits run faster);
+ *  - the tiled GEMM's operand stream alone: 32 KiB stages of 512 rows x 64
+ *    bytes moved into LDS by buffer_load_dwordx4 ... lds, two stages in
+ *    flight, a barrier per stage, 8 waves per workgroup, one workgroup per
+ *    CU.  Its rate per CU bounds how fast a CU can be fed 256 x 256 tiles.
  *
  * Conventions: device pointers, 16-byte aligned; `stream` is a hipStream_t
  * passed as void*; work is enqueued and the call returns at once.  Return
@@ -50,6 +54,13 @@ double mxc_mfma_loop_flops(int grid, int64_t iters);
  * `iters` iterations; out receives grid * 512 floats (each lane's sum of its
  * accumulators, so the work is not dead). */
 int mxc_mfma_loop(const void *operands, float *out, int grid, int64_t iters, void *stream);
+
+/* The LDS-DMA operand stream: `grid` workgroups each move `stages` stages of
+ * 32 KiB (grid * stages * 32768 bytes in all) from src, a device buffer of
+ * src_bytes (a multiple of 1 MiB: its 1 MiB windows are dealt to the
+ * workgroups round robin); out receives grid * 512 words read back from LDS,
+ * so the loads are not dead. */
+int mxc_lds_dma(const void *src, size_t src_bytes, uint32_t *out, int grid, int stages, void *stream);
 
 #ifdef __cplusplus
 }

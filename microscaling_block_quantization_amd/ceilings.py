@@ -1,8 +1,9 @@
 """Binding of libmx_ceilings.so (include/mx_ceilings.h): the context kernels the
 benchmark compares the hot path with -- a device copy, a read-mostly stream
-with the quantizer's 4:1 byte mix, and the FP4 matrix-instruction loop fed
-from LDS like the tiled GEMM.  Argument marshalling only; each function
-enqueues on the current torch stream and returns."""
+with the quantizer's 4:1 byte mix, the FP4 matrix-instruction loop fed from
+LDS like the tiled GEMM, and the GEMM's LDS-DMA operand stream on its own.
+Argument marshalling only; each function enqueues on the current torch
+stream and returns."""
 import ctypes
 import os
 
@@ -10,8 +11,10 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmx_ceilings.so")
-EXPORTS = ["mxc_copy", "mxc_read4_write1", "mxc_mfma_loop_grid", "mxc_mfma_loop_flops", "mxc_mfma_loop"]
+EXPORTS = ["mxc_copy", "mxc_read4_write1", "mxc_mfma_loop_grid", "mxc_mfma_loop_flops", "mxc_mfma_loop",
+           "mxc_lds_dma"]
 LOOP_OPERAND_BYTES = 32768
+DMA_STAGE_BYTES = 32768
 
 _lib = None
 
@@ -30,7 +33,8 @@ def lib():
         L.mxc_mfma_loop_flops.argtypes = [i32, i64]
         L.mxc_mfma_loop_flops.restype = ctypes.c_double
         L.mxc_mfma_loop.argtypes = [vp, vp, i32, i64, vp]
-        for n in ("mxc_copy", "mxc_read4_write1", "mxc_mfma_loop_grid", "mxc_mfma_loop"):
+        L.mxc_lds_dma.argtypes = [vp, sz, vp, i32, i32, vp]
+        for n in ("mxc_copy", "mxc_read4_write1", "mxc_mfma_loop_grid", "mxc_mfma_loop", "mxc_lds_dma"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -67,3 +71,9 @@ def mfma_loop(operands, out, grid, iters):
     assert operands.numel() * operands.element_size() >= LOOP_OPERAND_BYTES
     assert out.numel() >= grid * 512 and out.dtype == torch.float32
     _ok(lib().mxc_mfma_loop(operands.data_ptr(), out.data_ptr(), grid, iters, _s()), "mxc_mfma_loop")
+
+
+def lds_dma(src, out, grid, stages):
+    n = src.numel() * src.element_size()
+    assert out.numel() >= grid * 512 and out.element_size() == 4
+    _ok(lib().mxc_lds_dma(src.data_ptr(), n, out.data_ptr(), grid, stages, _s()), "mxc_lds_dma")

@@ -1,7 +1,8 @@
 // ceilings.hip -- context kernels for the measurement (libmx_ceilings.so,
 // include/mx_ceilings.h): a device copy, a read-mostly stream with the
-// quantizer's byte mix, and a loop of the block-scaled FP4 matrix instruction
-// fed from LDS like the tiled GEMM.  Nothing here is part of the method.
+// quantizer's byte mix, a loop of the block-scaled FP4 matrix instruction
+// fed from LDS like the tiled GEMM, and the GEMM's LDS-DMA operand stream on
+// its own.  Nothing here is part of the method.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -107,6 +108,45 @@ __global__ __launch_bounds__(64 * LOOP_WAVES, 1) void k_mfma_loop(const u32x4* _
     out[(int64_t)blockIdx.x * 64 * LOOP_WAVES + tid] = s;
 }
 
+// The LDS-DMA stream of the tiled GEMM without its arithmetic: each
+// workgroup of 8 waves moves `stages` stages of 32 KiB from global memory
+// into a 4-slot LDS ring with buffer_load_dwordx4 ... lds (16 bytes per lane).
+// A stage is 512 rows x 64 bytes of a window of 512 rows x 2048 bytes (the
+// 256 + 256 operand rows of one 256 x 256 output tile at K = 4096 in FP4):
+// each instruction moves 16 rows x 64 bytes, 4 per wave per stage; two stages
+// stay in flight and a barrier closes each stage, as in the GEMM.  The windows
+// (1 MiB each) are shared round robin by the workgroups, so after the first
+// pass they are read from the L2 / Infinity Cache, as the GEMM's panels are.
+constexpr int DMA_WAVES = 8;
+constexpr int DMA_STAGE = 32768;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(64 * DMA_WAVES, 1) void k_lds_dma(const uint8_t* __restrict__ src, int nwin, int stages,
+                                                              uint32_t* out) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * DMA_STAGE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* win = src + (size_t)(blockIdx.x % nwin) * (1u << 20);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(win), (short)0, 1 << 20,
+                                                                       0x00020000);
+    uint32_t acc = 0;
+    for (int st = 0; st < stages; st++) {
+        uint8_t* slot = ring + (st & 3) * DMA_STAGE;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int g = wave * 4 + k;                   // 16-row piece 0 .. 31
+            const int vo = (g * 16 + lane / 4) * 2048 + (st & 31) * 64 + (lane & 3) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + g * 1024), 16, vo, 0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // this wave's stage st - 2 has landed
+        __syncthreads();
+        acc += ring[(threadIdx.x * 64 + st * 4) % (4 * DMA_STAGE)];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    acc += ring[(threadIdx.x * 64) % (4 * DMA_STAGE)];
+    out[(int64_t)blockIdx.x * 64 * DMA_WAVES + threadIdx.x] = acc;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -147,6 +187,16 @@ int mxc_mfma_loop(const void* operands, float* out, int grid, int64_t iters, voi
     if (!operands || !out || grid <= 0 || iters <= 0 || !aligned16(operands)) return 1;
     k_mfma_loop<<<(unsigned)grid, 64 * LOOP_WAVES, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const u32x4*>(operands), out, iters);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int mxc_lds_dma(const void* src, size_t src_bytes, uint32_t* out, int grid, int stages, void* stream) {
+    if (!src || !out || grid <= 0 || stages <= 0 || src_bytes < (1u << 20) || src_bytes % (1u << 20) ||
+        !aligned16(src))
+        return 1;
+    const int nwin = (int)(src_bytes >> 20);
+    k_lds_dma<<<(unsigned)grid, 64 * DMA_WAVES, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint8_t*>(src), nwin, stages, out);
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -310,13 +310,18 @@ template <class G>
 __device__ __forceinline__ void load_scl(Scl<G>& o, const uint8_t* __restrict__ buf, int hf, int ra, int rb,
                                          int half) {
     const uint32_t sel = half ? 0x07030501u : 0x06020400u;
+    // all reads first, then the permutes: one LDS round trip, not one per row tile
+    u32x4v q[G::TI + G::TJ];
 #pragma unroll
     for (int i = 0; i < G::TI + G::TJ; i++) {
         const int off = i < G::TI ? (hf * G::BM + ra + 32 * i) * 16
                                   : G::BM * G::SROW + (hf * G::BN + rb + 32 * (i - G::TI)) * 16;
-        const u32x4v q = *reinterpret_cast<const u32x4v*>(buf + off);
-        o.p[i][0] = __builtin_amdgcn_perm(q.y, q.x, sel);
-        o.p[i][1] = __builtin_amdgcn_perm(q.w, q.z, sel);
+        q[i] = *reinterpret_cast<const u32x4v*>(buf + off);
+    }
+#pragma unroll
+    for (int i = 0; i < G::TI + G::TJ; i++) {
+        o.p[i][0] = __builtin_amdgcn_perm(q[i].y, q[i].x, sel);
+        o.p[i][1] = __builtin_amdgcn_perm(q[i].w, q[i].z, sel);
     }
 }
 
