@@ -263,6 +263,9 @@ def gemm_formats(mx, torch, a, b, C, R, dev, reps=5):
         ("NVFP4 x NVFP4", nv, nv, "fp16 MFMA after exact decode, LDS-staged 256x256 tiles", BF16_PEAK_TFLOPS),
         ("UE5M3/16 x UE5M3/16", F(scale=mx.SCALE_UE5M3, block_cols=16), F(scale=mx.SCALE_UE5M3, block_cols=16),
          "bf16 MFMA after exact decode, LDS-staged 256x256 tiles", BF16_PEAK_TFLOPS),
+        ("MBS/16 x MBS/16", F(block_cols=16, macro_cols=128), F(block_cols=16, macro_cols=128),
+         "bf16 MFMA after exact decode with the macro scale folded into each 1x16 block's, LDS-staged 256x256 tiles",
+         BF16_PEAK_TFLOPS),
     ]
     out = []
     for name, fa, fb, path, peak in cases:

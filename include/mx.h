@@ -231,8 +231,13 @@ int mx_qsnr(int dtype, const void *ref, const void *approx, int64_t n,
  *    is not of the kind above): the codes times their block scales are
  *    decoded exactly, to fp16 when both operands have UE4M3 scales and to
  *    bf16 otherwise, and the fp16 / bf16 matrix instruction multiplies.
+ *    Macro-block scales over E8M0 sub-blocks of other widths (the 1 x 128
+ *    macro over 1 x 16 blocks, [U] Sec. 4 MBS) take this route too, with E8M0
+ *    block scales on both operands: each block's scale is 2^e times its macro
+ *    block's UE4M3 scale (exact in fp32) and the decode applies it.
  * Anything else (INT4 / E3M0 elements, asymmetric, rotated, column or 2D
- * blocks, macro scales on FP6 / FP8): MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
+ * blocks, macro scales on FP6 / FP8 or against fp8 block scales):
+ * MX_ERR_UNSUPPORTED.  Shapes: K % 32 == 0 and
  * whole blocks (MX_ERR_ARG otherwise); any M, N.  E8M0 products with K a
  * multiple of 128 run on LDS-staged kernels (MXFP4 x MXFP4 without macro
  * scales and K a multiple of 1024 on the most tuned one), other K on a

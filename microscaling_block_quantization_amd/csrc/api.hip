@@ -367,13 +367,16 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
                         fb->block_cols == 32 && mxk::gemm_elem_ok(fa->elem) && mxk::gemm_elem_ok(fb->elem);
     if (!native) {
         // E2M1 under E8M0, UE4M3, NVFP4 or UE5M3 scales on any row block:
-        // decoded to bf16 for the bf16 matrix instruction
+        // decoded to bf16 for the bf16 matrix instruction.  Macro-block scales
+        // (MBS over E8M0 sub-blocks of other widths than 32, e.g. 1 x 16) fold
+        // into the decode; both operands then carry E8M0 block scales.
         for (const mx_format* f : {fa, fb})
-            if (f->elem != MX_ELEM_E2M1 || !mxk::gemm_upcvt_scale_ok(f->scale) || f->macro_cols)
-                return MX_ERR_UNSUPPORTED;
+            if (f->elem != MX_ELEM_E2M1 || !mxk::gemm_upcvt_scale_ok(f->scale)) return MX_ERR_UNSUPPORTED;
+        if ((fa->macro_cols || fb->macro_cols) && (fa->scale != MX_SCALE_E8M0 || fb->scale != MX_SCALE_E8M0))
+            return MX_ERR_UNSUPPORTED;
     }
-    // macro-block scales: MXFP4 operands only (the sub-blocks are the 1 x 32
-    // blocks the instruction scales)
+    // macro-block scales: E2M1 operands only (on the native route the
+    // sub-blocks are the 1 x 32 blocks the instruction scales)
     const bool mbs = fa->macro_cols || fb->macro_cols;
     if (mbs && (fa->elem != MX_ELEM_E2M1 || fb->elem != MX_ELEM_E2M1)) return MX_ERR_UNSUPPORTED;
     int rc = check_format(fa, a->rows, a->cols);
@@ -401,7 +404,9 @@ int mx_gemm(const mx_format* fa, const mx_qtensor* a, const mx_format* fb, const
     if (!native)
         return hip_status(mxk::launch_gemm_upcvt(
             fa->scale, fa->block_cols, ac, as, fa->scale == MX_SCALE_NVFP4 ? a->tensor_scale : nullptr, fb->scale,
-            fb->block_cols, bc, bs, fb->scale == MX_SCALE_NVFP4 ? b->tensor_scale : nullptr, c, M, N, K, ldc, cb, s));
+            fb->block_cols, bc, bs, fb->scale == MX_SCALE_NVFP4 ? b->tensor_scale : nullptr, c, M, N, K, ldc, cb, s,
+            fa->macro_cols ? static_cast<const uint8_t*>(a->macro_scales) : nullptr,
+            fb->macro_cols ? static_cast<const uint8_t*>(b->macro_scales) : nullptr));
     return hip_status(mxk::launch_gemm(fa->elem, ac, as, fb->elem, bc, bs, c, M, N, K, ldc, cb, s,
                                        fa->macro_cols ? static_cast<const uint8_t*>(a->macro_scales) : nullptr,
                                        fb->macro_cols ? static_cast<const uint8_t*>(b->macro_scales) : nullptr));

@@ -44,6 +44,7 @@ struct UOperand {
     const uint8_t* codes;     // rows x K/2 bytes
     const uint8_t* scales;    // rows x K/bc bytes
     int kind, bc;
+    const uint8_t* macro;     // nullable: UE4M3 macro-block scales, rows x K/128 bytes (E8M0 block scales only)
 };
 
 // value of a scale code: E8M0 2^(c - 127) (0xFF: NaN); UE4M3 / UE5M3 unsigned
@@ -102,10 +103,13 @@ __device__ __forceinline__ void load_row(bf8v (&o)[4], const UOperand& U, int64_
     const uint4 w = *reinterpret_cast<const uint4*>(U.codes + row * (K / 2) + kb / 2);
     const uint8_t* srow = U.scales + row * (K / U.bc);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    // macro-block scaling: the block's scale times the UE4M3 scale of its 1 x 128
+    // macro block (exact in fp32), and the fp32 decode
+    const float sm = U.macro ? uscale(U.macro[row * (K / 128) + kb / 128], UK_UE4M3) : 1.0f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const float sc = uscale(srow[(kb + 8 * j) / U.bc], U.kind);
-        o[j] = U.kind == UK_E8M0 ? decode8_pow2(ww[j], sc) : decode8(ww[j], sc);
+        o[j] = U.macro ? decode8(ww[j], sc * sm) : U.kind == UK_E8M0 ? decode8_pow2(ww[j], sc) : decode8(ww[j], sc);
     }
 }
 
@@ -203,8 +207,10 @@ constexpr int USTAGE = UCODES + (UBM + UBN) * 8;           // then 8 scale bytes
 constexpr int UPW = UCODES / 1024 / UNW;               // code DMA pieces per wave per stage
 constexpr int USW = (UBM + UBN) * 2 / 64 / UNW;        // scale DMA pieces (a dword per lane) per wave
 
-// operand decode kinds of the LDS kernel
-enum { DK_E8M0 = 0, DK_FP8 = 1, DK_F16 = 2 };
+// operand decode kinds of the LDS kernel: E8M0 by the scaled convert; fp8
+// scales, or E8M0 times a UE4M3 macro scale, by the fp32 decode; UE4M3 on both
+// sides by the fp16 route
+enum { DK_E8M0 = 0, DK_FP8 = 1, DK_F16 = 2, DK_MBS = 3 };
 
 __device__ __forceinline__ int uphys(int r, int p) { return p ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)); }
 
@@ -221,7 +227,9 @@ struct UDec {
 
 struct UPanels {
     rsrc_t a, b, sa, sb, z;
+    rsrc_t ma, mb;                                      // macro scale panels (DK_MBS operands)
     int rowb, srowa, srowb, spa, spb, nst;              // code row bytes; scale row and stage bytes of A, B
+    int mrow;                                           // macro bytes per row (K / 128)
 };
 
 template <int N>
@@ -293,7 +301,7 @@ __device__ __forceinline__ h8v dec8_f16(uint32_t w, h2v h) {
 // (s * 2^-8, the exponent bias difference) in both halves
 template <int DK>
 __device__ __forceinline__ uint32_t uscale_bits(uint32_t c, const UDec& d) {
-    if constexpr (DK == DK_E8M0) {
+    if constexpr (DK == DK_E8M0 || DK == DK_MBS) {
         const uint32_t v = c ? c << 23 : 0x00400000u;
         return c == 255u ? 0x7fc00000u : v;
     } else if constexpr (DK == DK_FP8) {
@@ -310,11 +318,23 @@ struct UVec {
     typedef typename std::conditional<DK == DK_F16, h8v, bf8v>::type type;
 };
 
+// sm: the macro scale of the row's current macro block (DK_MBS; else unused)
 template <int DK>
-__device__ __forceinline__ typename UVec<DK>::type udecode(uint32_t w, uint32_t sb) {
+__device__ __forceinline__ typename UVec<DK>::type udecode(uint32_t w, uint32_t sb, float sm) {
     if constexpr (DK == DK_E8M0) return decode8_pow2(w, __uint_as_float(sb));
     else if constexpr (DK == DK_FP8) return decode8(w, __uint_as_float(sb));
+    else if constexpr (DK == DK_MBS) return decode8(w, __uint_as_float(sb) * sm);
     else return dec8_f16(w, __builtin_bit_cast(h2v, sb));
+}
+
+// the UE4M3 macro scales of this lane's row tiles for one 128-wide stage: one
+// byte per row, read through a resource over the tile's valid rows (rows past
+// the end read as 0)
+template <int R>
+__device__ __forceinline__ void load_macro(float (&m)[R], rsrc_t r, int row0, int mrow, int s) {
+#pragma unroll
+    for (int i = 0; i < R; i++)
+        m[i] = uscale((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (row0 + 32 * i) * mrow + s, 0, 0), UK_UE4M3);
 }
 
 // the scale byte of group q (8 codes) of this lane's chunk, from the chunk's
@@ -323,11 +343,18 @@ __device__ __forceinline__ uint32_t ugroup_code(uint32_t x, int q, int lg) {
     return (x >> (8 * ((q >> 1) & (lg == 4 ? 1 : 0)))) & 0xffu;
 }
 
+// One stage.  With macro scales (DK_MBS), ma / mb hold the stage's macro
+// values; the next stage's are loaded after the barrier, before the DMA of
+// stage s + 2, so the wait of the next step (for stage s + 1, with the DMA of
+// s + 2 in flight) covers them.
 template <int KA, int KB>
 __device__ __forceinline__ void ustep(uint8_t* smem, const UPanels& P, int s, int wave, int lane, int half, int ra,
-                                      int rb, const UDec& da, const UDec& db, v16f (&acc)[UTI][UTJ]) {
+                                      int rb, const UDec& da, const UDec& db, v16f (&acc)[UTI][UTJ],
+                                      float (&ma)[UTI], float (&mb)[UTJ], float (&na)[UTI], float (&nb)[UTJ]) {
     uwait_vm<UPW + USW>();
     ubarrier();
+    if constexpr (KA == DK_MBS) load_macro<UTI>(na, P.ma, ra, P.mrow, s + 1 < P.nst ? s + 1 : s);
+    if constexpr (KB == DK_MBS) load_macro<UTJ>(nb, P.mb, rb, P.mrow, s + 1 < P.nst ? s + 1 : s);
     ustage_dma(smem, P, s + 2, wave, lane);
     const uint8_t* st = smem + (s % UD) * USTAGE;
 #pragma unroll
@@ -358,10 +385,10 @@ __device__ __forceinline__ void ustep(uint8_t* smem, const UPanels& P, int s, in
             typename UVec<KB>::type b[UTJ];
 #pragma unroll
             for (int i = 0; i < UTI; i++)
-                a[i] = udecode<KA>(xa[i][q], uscale_bits<KA>(ugroup_code(ca[i], q, da.lg), da));
+                a[i] = udecode<KA>(xa[i][q], uscale_bits<KA>(ugroup_code(ca[i], q, da.lg), da), ma[i]);
 #pragma unroll
             for (int j = 0; j < UTJ; j++)
-                b[j] = udecode<KB>(xb[j][q], uscale_bits<KB>(ugroup_code(cb[j], q, db.lg), db));
+                b[j] = udecode<KB>(xb[j][q], uscale_bits<KB>(ugroup_code(cb[j], q, db.lg), db), mb[j]);
 #pragma unroll
             for (int i = 0; i < UTI; i++)
 #pragma unroll
@@ -379,7 +406,7 @@ template <bool CBF16, int KA, int KB>
 __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_upcvt_lds(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, UDec da, UDec db, const float* ta, const float* tb, void* __restrict__ C,
-    int64_t M, int64_t N, int64_t K, int64_t ldc) {
+    int64_t M, int64_t N, int64_t K, int64_t ldc, const uint8_t* __restrict__ MA, const uint8_t* __restrict__ MB) {
     static_assert((KA == DK_F16) == (KB == DK_F16), "the fp16 route needs both operands in fp16");
     __shared__ __attribute__((aligned(16))) uint8_t smem[UD * USTAGE];
     const int lane = threadIdx.x & 63;
@@ -411,6 +438,9 @@ __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))
     P.spa = 128 >> da.lg;
     P.spb = 128 >> db.lg;
     P.nst = (int)(K / 128);
+    P.mrow = (int)(K / 128);
+    P.ma = KA == DK_MBS ? ursrc(MA + m0 * P.mrow, va * P.mrow) : P.z;
+    P.mb = KB == DK_MBS ? ursrc(MB + n0 * P.mrow, vb * P.mrow) : P.z;
 
     const int ra = wm * 32 * UTI + lrow, rb = wn * 32 * UTJ + lrow;
     v16f acc[UTI][UTJ];
@@ -420,9 +450,23 @@ __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int j = 0; j < UTJ; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    // macro scales of stage 0 go out before its DMA, so its wait covers them
+    float ma[UTI], mb[UTJ], na[UTI], nb[UTJ];
+#pragma unroll
+    for (int i = 0; i < UTI; i++) ma[i] = na[i] = 1.0f;
+#pragma unroll
+    for (int j = 0; j < UTJ; j++) mb[j] = nb[j] = 1.0f;
+    if constexpr (KA == DK_MBS) load_macro<UTI>(ma, P.ma, ra, P.mrow, 0);
+    if constexpr (KB == DK_MBS) load_macro<UTJ>(mb, P.mb, rb, P.mrow, 0);
     ustage_dma(smem, P, 0, wave, lane);
     ustage_dma(smem, P, 1, wave, lane);
-    for (int s = 0; s < P.nst; s++) ustep<KA, KB>(smem, P, s, wave, lane, half, ra, rb, da, db, acc);
+    for (int s = 0; s < P.nst; s++) {
+        ustep<KA, KB>(smem, P, s, wave, lane, half, ra, rb, da, db, acc, ma, mb, na, nb);
+#pragma unroll
+        for (int i = 0; i < UTI; i++) ma[i] = na[i];
+#pragma unroll
+        for (int j = 0; j < UTJ; j++) mb[j] = nb[j];
+    }
     uwait_vm<0>();
 
     const float g = (ta ? *ta : 1.0f) * (tb ? *tb : 1.0f);
@@ -458,15 +502,23 @@ hipError_t launch_upcvt_lds_t(const UOperand& A, const UOperand& B, const float*
     const UDec da = udec(A), db = udec(B);
     if (c_bf16)
         k_gemm_upcvt_lds<true, KA, KB><<<(unsigned)tiles, 64 * UNW, 0, s>>>(A.codes, A.scales, B.codes, B.scales, da,
-                                                                          db, ta, tb, c, M, N, K, ldc);
+                                                                          db, ta, tb, c, M, N, K, ldc, A.macro, B.macro);
     else
         k_gemm_upcvt_lds<false, KA, KB><<<(unsigned)tiles, 64 * UNW, 0, s>>>(A.codes, A.scales, B.codes, B.scales, da,
-                                                                           db, ta, tb, c, M, N, K, ldc);
+                                                                           db, ta, tb, c, M, N, K, ldc, A.macro,
+                                                                           B.macro);
     return hipGetLastError();
 }
 
 hipError_t launch_upcvt_lds(const UOperand& A, const UOperand& B, const float* ta, const float* tb, void* c,
                             int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+    // macro-block scaled operands (E8M0 block scales) against E8M0 ones
+    if (A.macro || B.macro) {
+        if (A.kind != UK_E8M0 || B.kind != UK_E8M0) return hipErrorInvalidValue;
+        if (A.macro && B.macro) return launch_upcvt_lds_t<DK_MBS, DK_MBS>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+        if (A.macro) return launch_upcvt_lds_t<DK_MBS, DK_E8M0>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+        return launch_upcvt_lds_t<DK_E8M0, DK_MBS>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
+    }
     if (A.kind == UK_UE4M3 && B.kind == UK_UE4M3)
         return launch_upcvt_lds_t<DK_F16, DK_F16>(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
     const bool pa = A.kind == UK_E8M0, pb = B.kind == UK_E8M0;
@@ -484,12 +536,14 @@ bool gemm_upcvt_scale_ok(int scale) {
 
 hipError_t launch_gemm_upcvt(int sca, int bca, const uint8_t* a, const uint8_t* sa, const float* ta, int scb, int bcb,
                              const uint8_t* b, const uint8_t* sb, const float* tb, void* c, int64_t M, int64_t N,
-                             int64_t K, int64_t ldc, int c_bf16, hipStream_t s) {
+                             int64_t K, int64_t ldc, int c_bf16, hipStream_t s, const uint8_t* ma,
+                             const uint8_t* mb) {
     if (M == 0 || N == 0) return hipSuccess;
     if (!gemm_upcvt_scale_ok(sca) || !gemm_upcvt_scale_ok(scb) || bca % 8 || bcb % 8 || K % 32)
         return hipErrorInvalidValue;
-    const UOperand A = {a, sa, ukind(sca), bca};
-    const UOperand B = {b, sb, ukind(scb), bcb};
+    if ((ma || mb) && (K % 128 || sca != SC_E8M0 || scb != SC_E8M0)) return hipErrorInvalidValue;
+    const UOperand A = {a, sa, ukind(sca), bca, ma};
+    const UOperand B = {b, sb, ukind(scb), bcb, mb};
     if (K % 128 == 0 && (bca == 16 || bca == 32) && (bcb == 16 || bcb == 32))
         return launch_upcvt_lds(A, B, ta, tb, c, M, N, K, ldc, c_bf16, s);
     dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));

@@ -73,10 +73,13 @@ hipError_t launch_gemm_lds(int ea, const uint8_t* a, const uint8_t* sa, int eb, 
                            void* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int c_bf16, hipStream_t s,
                            const uint8_t* ma = nullptr, const uint8_t* mb = nullptr);
 // E2M1 operands under E8M0 / UE4M3 / NVFP4 / UE5M3 scales on 1 x bc blocks
-// (bc a multiple of 8), decoded to bf16; ta / tb: per-tensor scales or null
+// (bc a multiple of 8), decoded to bf16; ta / tb: per-tensor scales or null;
+// ma / mb: UE4M3 macro-block scales per 1 x 128 (E8M0 block scales on both
+// operands, K % 128 == 0), nullable
 bool gemm_upcvt_scale_ok(int scale);
 hipError_t launch_gemm_upcvt(int sca, int bca, const uint8_t* a, const uint8_t* sa, const float* ta, int scb, int bcb,
                              const uint8_t* b, const uint8_t* sb, const float* tb, void* c, int64_t M, int64_t N,
-                             int64_t K, int64_t ldc, int c_bf16, hipStream_t s);
+                             int64_t K, int64_t ldc, int c_bf16, hipStream_t s, const uint8_t* ma = nullptr,
+                             const uint8_t* mb = nullptr);
 
 }  // namespace mxk

@@ -202,6 +202,20 @@ def test_gemm_rejects_before_launch():
     am = mx.MxQTensor(1024, 2048, None, 4096, None, None, 64, 256)
     assert L.mx_gemm(ctypes.byref(fm), ctypes.byref(am), ctypes.byref(f), ctypes.byref(b), 0x10008, 32,
                      mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
+    # macro scales over 1 x 16 E8M0 sub-blocks (the decode route): against fp8
+    # block scales not run; without the macro buffer an argument error;
+    # otherwise through validation (misaligned C, so no launch)
+    fm16 = mx.Format(macro_cols=128, block_cols=16).c()
+    a16 = mx.MxQTensor(1024, 2048, None, None, None, None, 64, 256)
+    b16 = mx.MxQTensor(4096, 8192, None, 12288, None, None, 32, 256)
+    a16m = mx.MxQTensor(1024, 2048, None, 4096, None, None, 64, 256)
+    nv16 = mx.Format(scale=mx.SCALE_UE4M3, block_cols=16).c()
+    assert L.mx_gemm(ctypes.byref(fm16), ctypes.byref(a16m), ctypes.byref(nv16), ctypes.byref(b16), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mx_gemm(ctypes.byref(fm16), ctypes.byref(a16), ctypes.byref(fm16), ctypes.byref(b16), 0x10000, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ARG
+    assert L.mx_gemm(ctypes.byref(fm16), ctypes.byref(a16m), ctypes.byref(fm16), ctypes.byref(b16), 0x10008, 32,
+                     mx.DTYPE_BF16, None) == mx.MX_ERR_ALIGN
     # FP6 elements need E8M0 scales on 1 x 32 blocks; NVFP4 needs its tensor scale
     g6u = mx.Format(elem=mx.ELEM_FP6_E2M3, scale=mx.SCALE_UE4M3, block_cols=16).c()
     assert L.mx_gemm(ctypes.byref(g6u), ctypes.byref(a), ctypes.byref(f), ctypes.byref(b), 0x10000, 32,

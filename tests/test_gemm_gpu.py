@@ -383,6 +383,98 @@ def test_mbs_quantized_operands():
     assert db_mbs > db_4
 
 
+# ---- MBS over E8M0 sub-blocks of other widths (c4's 1 x 128 macro over 1 x 16) ----
+# The scaled instruction takes one power-of-two scale per 32 K-values, so these
+# products go through the decode kernels: each block's scale is 2^e times its
+# macro block's UE4M3 scale, exact in fp32, and the decode applies it.
+def mbs_operand(rng, rows, K, bc, macro_codes):
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(118, 137, (rows, K // bc), dtype=np.uint8)
+    mac = rng.choice(np.asarray(macro_codes, np.uint8), (rows, K // 128))
+    fo = oracle.Format(block_cols=bc, macro_cols=128)
+    deq = oracle.dequantize(fo, {"codes": codes, "scales": scales, "macro_scales": mac}, rows, K)
+    q = make_q(codes, scales, rows, K)
+    q.macro_scales = torch.from_numpy(mac.reshape(-1).copy()).cuda()
+    return q, deq, mx.Format(block_cols=bc, macro_cols=128)
+
+
+@pytest.mark.parametrize("sides", ["both", "a", "b"])
+@pytest.mark.parametrize("bc,M,N,K", [(16, 130, 200, 1024), (16, 257, 33, 128), (16, 64, 300, 384),
+                                      (32, 200, 70, 256), (64, 96, 130, 512), (8, 40, 50, 256)])
+def test_mbs_sub_blocks_random(sides, bc, M, N, K):
+    """Random codes, E8M0 block scales over 1 x bc sub-blocks and UE4M3 macro
+    scales of 1 .. 2 (the quantizer's range) on one or both operands; the other
+    operand plain E8M0 1 x bc (LDS-staged decode kernel for bc 16 and 32 when
+    the plain side is 1 x 16 / 1 x 32, register-only otherwise).  fp32 output
+    within 1e-5 relative Frobenius of the fp64 oracle product, bf16 output
+    within 1e-3."""
+    rng = np.random.default_rng(bc * 1000 + M + K)
+    macro = list(range(0x38, 0x41))
+    if sides in ("both", "a"):
+        qa, da, fa = mbs_operand(rng, M, K, bc, macro)
+    else:
+        ca, sa = rng.integers(0, 256, (M, K // 2), dtype=np.uint8), rng.integers(118, 137, (M, K // bc), dtype=np.uint8)
+        qa, fa = make_q(ca, sa, M, K), mx.Format(block_cols=bc)
+        da = oracle.dequantize(oracle.Format(block_cols=bc), {"codes": ca, "scales": sa}, M, K)
+    if sides in ("both", "b"):
+        qb, db, fb = mbs_operand(rng, N, K, bc, macro)
+    else:
+        cb, sb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8), rng.integers(118, 137, (N, K // bc), dtype=np.uint8)
+        qb, fb = make_q(cb, sb, N, K), mx.Format(block_cols=bc)
+        db = oracle.dequantize(oracle.Format(block_cols=bc), {"codes": cb, "scales": sb}, N, K)
+    ref = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    c16 = mx.mx_gemm(fa, qa, fb, qb).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert rel_frob(c32, ref) <= 1e-5
+    assert rel_frob(oracle.bf16_bits_to_f32(c16), oracle.bf16_bits_to_f32(bf16_of(ref))) <= 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 200, 512), (33, 65, 256)])
+def test_mbs_sub_blocks_exact_case(M, N, K):
+    """Unit block scales and macro scales of 1 and 2 over 1 x 16 sub-blocks:
+    every partial sum is a multiple of 1/4 below 2^24 in magnitude, so the fp32
+    result equals the oracle's exact product bit for bit."""
+    rng = np.random.default_rng(K + 17)
+    qa, _, fa = mbs_operand(rng, M, K, 16, [0x38, 0x40])
+    qb, _, fb = mbs_operand(rng, N, K, 16, [0x38, 0x40])
+    for q in (qa, qb):
+        q.scales.fill_(127)
+    fo = oracle.Format(block_cols=16, macro_cols=128)
+    da = oracle.dequantize(fo, {"codes": qa.codes.cpu().numpy().reshape(M, K // 2),
+                                "scales": qa.scales.cpu().numpy().reshape(M, K // 16),
+                                "macro_scales": qa.macro_scales.cpu().numpy().reshape(M, K // 128)}, M, K)
+    db = oracle.dequantize(fo, {"codes": qb.codes.cpu().numpy().reshape(N, K // 2),
+                                "scales": qb.scales.cpu().numpy().reshape(N, K // 16),
+                                "macro_scales": qb.macro_scales.cpu().numpy().reshape(N, K // 128)}, N, K)
+    exact = oracle.gemm_f64(da, db)
+    c32 = mx.mx_gemm(fa, qa, fb, qb, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(c32, exact.astype(np.float32))
+
+
+def test_mbs_sub_blocks_quantized_operands():
+    """c4's MBS format (1 x 128 UE4M3 macro over 1 x 16 E8M0 blocks) quantized
+    on the GPU from activation-like and weight-like tensors, then multiplied:
+    the product against the oracle's dequantized product, and its fidelity
+    (eq. (2)) above plain 1 x 16 E8M0 blocks without the macro scales."""
+    a, b = synth.w5(m=256, n=384, k=1024)
+    f16m = mx.Format(block_cols=16, macro_cols=128)
+    qa, _, _ = mx.mx_quantize(f16m, to_dev(a))
+    qb, _, _ = mx.mx_quantize(f16m, to_dev(b))
+    fo = oracle.Format(block_cols=16, macro_cols=128)
+    ra, rb = oracle.quantize(a, fo), oracle.quantize(b, fo)
+    ref = oracle.gemm_f64(ra["dequant"], rb["dequant"])
+    c32 = mx.mx_gemm(f16m, qa, f16m, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_frob(c32.cpu().numpy(), ref) <= 1e-5
+    R = oracle.gemm_f64(synth.bf16_bits_to_f32(a), synth.bf16_bits_to_f32(b)).astype(np.float32)
+    _, db_mbs = oracle.qsnr(R, c32.cpu().numpy())
+    f16 = mx.Format(block_cols=16)
+    pa, _, _ = mx.mx_quantize(f16, to_dev(a))
+    pb, _, _ = mx.mx_quantize(f16, to_dev(b))
+    _, db_16 = oracle.qsnr(R, mx.mx_gemm(f16, pa, f16, pb, out_dtype=torch.float32).cpu().numpy())
+    assert db_mbs > db_16
+
+
 # ---- FP4 under UE4M3 / NVFP4 / UE5M3 / non-32 E8M0 blocks: bf16 decode path ----
 # (scale kind, block, unit scale code, codes drawn for random scales)
 UPC = {"nvfp4": (oracle.SC_NVFP4, 16, 0x38, (0x28, 0x48)), "ue4m3": (oracle.SC_UE4M3, 16, 0x38, (0x28, 0x48)),
