@@ -156,7 +156,13 @@ typedef struct mx_stats {
 } mx_stats;
 
 /* Byte sizes of every output of mx_quantize for this format and shape, and of
- * the device workspace it needs (zero when it needs none).  `out` is host.  */
+ * the device workspace it needs (zero when it needs none).  `out` is host.
+ * The storage is the format's bit budget: codes at the element width plus one
+ * scale byte per block, 4 + 8/32 = 4.25 bits per element for 1 x 32 blocks
+ * and 4.5 for 1 x 16 ([U] Sec. 3); plus the bf16 offsets, the macro scales
+ * (one byte per 1 x 128), the fp32 tensor scale or the int32 reference
+ * exponent where the format has them.  Returns MX_ERR_ARG / MX_ERR_UNSUPPORTED
+ * for a format or shape mx_quantize would reject; `out` is then untouched.  */
 typedef struct mx_sizes {
     size_t codes, scales, offsets, macro_scales, tensor_scale, ref_exp, workspace;
 } mx_sizes;
@@ -200,7 +206,15 @@ int mx_quantize_noalloc(const mx_format *f, int in_dtype, const void *x, int64_t
                         int64_t cols, int64_t ld, const mx_qtensor *out, void *dequant,
                         int dq_dtype, mx_stats *stats, void *stream);
 
-/* Dequantize q into y (rows x cols, row stride ld elements, dtype out_dtype). */
+/* Dequantize q into y (rows x cols, row stride ld elements, dtype out_dtype
+ * MX_DTYPE_F32 or MX_DTYPE_BF16, rounded to nearest even): each element is its
+ * code's value times its block's scale (plus the block's offset when
+ * asymmetric, times the macro scale under MBS, times the tensor scale for
+ * NVFP4), the value mx_quantize's dequant output and statistics use.  This is
+ * the fake (simulated) quantization with which [A] (research flow step 1)
+ * studies MX formats on hardware that does not run them.  A block whose scale
+ * code is NaN dequantizes to NaN.  q's buffers as mx_quantize wrote them;
+ * ld >= cols with ld * element size a multiple of 16 (MX_ERR_ALIGN).        */
 int mx_dequantize(const mx_format *f, const mx_qtensor *q, int out_dtype, void *y,
                   int64_t ld, void *stream);
 
