@@ -745,6 +745,32 @@ struct HwArgs {
     float hconst;            // fp32 rounding of 1 / sqrt(h)
 };
 
+// a / b rounded to nearest even, given r = the correctly rounded 1 / b:
+// Markstein's correction step, q = a r, e = a - q b (exact, one FMA), then
+// q + e r.  It is the correctly rounded quotient whenever no intermediate
+// leaves the normal range: for |a| >= 2^-96 and a quotient of at least 2^-96
+// (checked on the CPU against the exact quotient for every finite bf16 input
+// and every UE4M3 / UE5M3 divisor, the macro scales 1 .. 2, and 8e7 random
+// fp32 divisors); smaller quotients keep their sign and stay below 2^-80, far
+// under any E2M1 rounding point.  The sign of a zero is a's.
+__device__ __forceinline__ float div_by(float a, float b, float r) {
+    const float q = a * r;
+    const float e = __builtin_fmaf(-q, b, a);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q), a);
+}
+// true in every lane when some lane's value is nonzero and below 2^-96, or
+// not finite: the chunk then divides exactly
+template <int N>
+__device__ __forceinline__ bool wave_needs_exact_div(const float (&v)[N]) {
+    bool sp = false;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const uint32_t u = __float_as_uint(v[i]) & 0x7fffffffu;
+        sp = sp || (u != 0u && u < 0x0f800000u) || u >= 0x7f800000u;
+    }
+    return __any(sp);
+}
+
 // the value of lane l ^ S of the wave (S a power of two below 32)
 template <int S>
 __device__ __forceinline__ float xlane(float v) {
@@ -885,8 +911,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                     smc = (uint32_t)fp8_code(false, mu);
                     sM = fp8_value(false, (int)smc);
                 }
+                if (wave_needs_exact_div(x)) {
 #pragma unroll
-                for (int i = 0; i < EPC; i++) y[i] = x[i] / sM;
+                    for (int i = 0; i < EPC; i++) y[i] = x[i] / sM;
+                } else {
+                    const float rM = 1.0f / sM;
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) y[i] = div_by(x[i], sM, rM);
+                }
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)smc, rm, lmc + k * (64 / h.mg), 0, 0);
             } else {
 #pragma unroll
@@ -919,8 +951,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 const float sb = fp8_value(h.ue5 != 0, sc);
                 const float S = h.nvfp4 ? sb * gts : sb;
                 float v[EPC];
+                if (wave_needs_exact_div(y)) {
 #pragma unroll
-                for (int i = 0; i < EPC; i++) v[i] = S == 0.f ? ((__float_as_uint(y[i]) >> 31) ? -0.f : 0.f) : y[i] / S;
+                    for (int i = 0; i < EPC; i++) v[i] = y[i] / S;
+                } else {
+                    const float rS = 1.0f / S;
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) v[i] = div_by(y[i], S, rS);
+                }
+#pragma unroll
+                for (int i = 0; i < EPC; i++)
+                    if (S == 0.f) v[i] = (__float_as_uint(y[i]) >> 31) ? -0.f : 0.f;
                 cw = enc_fp4<EPC / 2>(v, 1.0f);
                 if (nonfinite) cw = 0;
                 dec_fp4<EPC / 2>(cw, 1.0f, d);
