@@ -748,11 +748,12 @@ struct HwArgs {
 // a / b rounded to nearest even, given r = the correctly rounded 1 / b:
 // Markstein's correction step, q = a r, e = a - q b (exact, one FMA), then
 // q + e r.  It is the correctly rounded quotient whenever no intermediate
-// leaves the normal range: for |a| >= 2^-96 and a quotient of at least 2^-96
-// (checked on the CPU against the exact quotient for every finite bf16 input
-// and every UE4M3 / UE5M3 divisor, the macro scales 1 .. 2, and 8e7 random
-// fp32 divisors); smaller quotients keep their sign and stay below 2^-80, far
-// under any E2M1 rounding point.  The sign of a zero is a's.
+// leaves the normal range: for |a| >= 2^-96 and a quotient in [2^-96, 2^120]
+// (a block's quotients never exceed max(8, amax / 448); by the macro scales
+// 1 .. 2 over the whole range); smaller quotients keep their sign and stay
+// below 2^-80, far under any E2M1 rounding point.  The sign of a zero is a's.
+// tests/test_division_identity.py emulates the sequence exactly and checks it
+// against every finite bf16 input and every UE4M3 / UE5M3 and macro divisor.
 __device__ __forceinline__ float div_by(float a, float b, float r) {
     const float q = a * r;
     const float e = __builtin_fmaf(-q, b, a);
