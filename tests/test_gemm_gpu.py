@@ -105,16 +105,18 @@ def exact_k(ea, eb, cap):
     return min(cap, int((2 ** 24 - 1) // per) // 32 * 32)
 
 
-# Precision of the block-scaled matrix instruction, measured on gfx950 with
-# single-instruction probes: products are added in fixed point, keeping about
-# 14 bits below the leading bit of the largest product (bits below are dropped
-# toward zero), and the instruction results accumulate in fp32.  E2M1, E2M3 and
+# Precision of the block-scaled matrix instruction, measured on gfx950
+# (test_fp6_instruction_window_measured below): the products of each 32-wide
+# scale block are added in fixed point, keeping 14 bits below the leading bit
+# of the block's largest product (bits below are dropped toward zero); the two
+# block sums and the instruction results accumulate in fp32.  E2M1, E2M3 and
 # every pair other than E3M2 x E3M2 have no product bits that far down (their
 # smallest product step is at least 2^-14 of their largest product), so those
 # are exact.  E3M2 x E3M2 products span 2^-8 .. 784 (18 binades) and lose the
 # low bits of small products summed with large ones: each of an instruction's
 # 64 products, and each of its partial sums, loses less than one unit of
-# 2^(E - 14), E = floor(log2) of the instruction's largest product magnitude.
+# 2^(E - 14), E = floor(log2) of the instruction's largest product magnitude
+# (a bound that also covers the per-block window).
 MFMA_WINDOW = 14
 TRUNCATING = {("e3m2", "e3m2")}
 
@@ -135,6 +137,52 @@ def window_bound(deq_a, deq_b):
         unit = np.where(top > 0, np.exp2(np.floor(np.log2(np.where(top > 0, top, 1.0))) - MFMA_WINDOW), 0.0)
         out[m0:m0 + 16] = 72.0 * unit.sum(axis=2)
     return out
+
+
+def test_fp6_instruction_window_measured():
+    """The fixed-point window behind MFMA_WINDOW, measured through mx_gemm with
+    one 64-wide K step (one matrix instruction per output), FP6 E3M2 operands
+    under unit scales (the oracle's quantization of the values below, exact):
+    every output is 28 x 28 = 784 (leading bit 2^9) plus one product p of the
+    same 32-wide block, p = +-2^e x (1 or 2^-4), so |p| runs from 2^-8 to 2^3.
+    A product of at least 2^(9 - 14) is kept exactly.  A positive smaller one
+    is dropped (the sum stays 784); a negative one changes the sum by at most
+    one unit of 2^(9 - 14).  (A small product in another block of the same
+    instruction is kept: each block's products are summed on their own and
+    the block sums are added in fp32.)"""
+    M, N, K = 16, 8, 64
+    es = np.arange(-4, 4)
+    a = np.zeros((M, K), np.float32)
+    b = np.zeros((N, K), np.float32)
+    a[:, 0] = 28.0
+    b[:, 0] = 28.0
+    a[:8, 1] = np.exp2(es)
+    a[8:, 1] = -np.exp2(es)
+    b[:4, 1] = 1.0
+    b[4:, 1] = 0.0625
+    a[:, 33] = 2.0 ** -4            # the same small product in the second block: always kept
+    b[:, 33] = 2.0 ** -4
+    fo = oracle.Format(elem=oracle.FP6_E3M2)
+    ra, rb = oracle.quantize(a, fo), oracle.quantize(b, fo)
+    assert np.array_equal(ra["dequant"], a) and np.array_equal(rb["dequant"], b)
+    fm = mx.Format(elem=oracle.FP6_E3M2)
+    qa = make_q(ra["codes"], ra["scales"], M, K)
+    qb = make_q(rb["codes"], rb["scales"], N, K)
+    c = mx.mx_gemm(fm, qa, fm, qb, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    other = 2.0 ** -8                 # the second block's product
+    low = 9 - MFMA_WINDOW
+    unit = 2.0 ** low
+    for i in range(M):
+        for j in range(N):
+            p = float(a[i, 1]) * float(b[j, 1])
+            got = c[i, j] - 784.0 - other
+            if abs(p) >= unit:
+                assert got == p, (i, j, p, got)
+            elif p > 0:
+                assert got == 0.0, (i, j, p, got)
+            else:
+                assert -unit <= got <= 0.0, (i, j, p, got)
+    print("kept from 2^%d on; e.g. p = 2^-6 ->" % low, c[0, 4] - 784.0 - other)
 
 
 @pytest.mark.parametrize("ea,eb", PAIRS)
