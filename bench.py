@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-formats", action="store_true",
                     help="skip the other quantizer cells and GEMM formats (not part of the step)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the context ceilings")
+    ap.add_argument("--only-gemm-formats", action="store_true",
+                    help="only the products in the other block formats (gemm_formats), for a kernel trace")
     ap.add_argument("--only-formats", action="store_true",
                     help="run only the quantizer cells (for profiling them)")
     return ap.parse_args()
@@ -266,6 +268,8 @@ def gemm_formats(mx, torch, a, b, C, R, dev, reps=5):
         ("MBS/16 x MBS/16", F(block_cols=16, macro_cols=128), F(block_cols=16, macro_cols=128),
          "bf16 MFMA after exact decode with the macro scale folded into each 1x16 block's, LDS-staged 256x256 tiles",
          BF16_PEAK_TFLOPS),
+        ("MXFP8 E4M3 x MXFP8 E4M3", mx.MXFP8_E4M3, mx.MXFP8_E4M3, "fp8 MFMA, LDS-staged 256x256 tiles", FP8_PEAK_TFLOPS),
+        ("MXFP8 E4M3 x MXFP4", mx.MXFP8_E4M3, mx.MXFP4, "fp8 x fp4 MFMA, LDS-staged 256x256 tiles", FP8_PEAK_TFLOPS),
     ]
     out = []
     for name, fa, fb, path, peak in cases:
@@ -323,6 +327,13 @@ def main():
 
     def up(x):
         return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.only_gemm_formats:
+        a_t, b_t = up(a_np), up(b_np)
+        c_t = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        r_t = torch.matmul(a_t, b_t.t().contiguous()).float()
+        print(json.dumps({"gemm_formats": gemm_formats(mx, torch, a_t, b_t, c_t, r_t, dev)}), flush=True)
+        return
 
     A = [up(a_np)]
     B = [up(b_np)]
