@@ -761,15 +761,31 @@ __device__ __forceinline__ float div_by(float a, float b, float r) {
 }
 // true in every lane when some lane's value is nonzero and below 2^-96, or
 // not finite: the chunk then divides exactly
+// (the magnitudes' minimum after u - 1, which wraps zero to the top, finds a
+// nonzero one below 2^-96; their maximum finds a non-finite one)
 template <int N>
 __device__ __forceinline__ bool wave_needs_exact_div(const float (&v)[N]) {
-    bool sp = false;
+    uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
     for (int i = 0; i < N; i++) {
         const uint32_t u = __float_as_uint(v[i]) & 0x7fffffffu;
-        sp = sp || (u != 0u && u < 0x0f800000u) || u >= 0x7f800000u;
+        lo = min(lo, u - 1u);
+        hi = max(hi, u);
     }
-    return __any(sp);
+    return __any(lo < 0x0f7fffffu || hi >= 0x7f800000u);
+}
+
+// a / b rounded to nearest even for one value per lane, through div_by with
+// r = RN(1/b) when every lane's dividend is zero, not finite, or in [2^-90,
+// 2^119] with RN(a r) in [2^-94, 2^118] (then the quotient lies inside
+// div_by's range), else by the exact divide
+__device__ __forceinline__ float div_lane(float a, float b, float r) {
+    const uint32_t u = __float_as_uint(a) & 0x7fffffffu;
+    const uint32_t q = __float_as_uint(a * r) & 0x7fffffffu;
+    const bool ok = u == 0u || u >= 0x7f800000u ||
+                    (u >= 0x12800000u && u <= 0x7b000000u && q >= 0x10800000u && q <= 0x7a800000u);
+    if (__all(ok)) return div_by(a, b, r);
+    return a / b;
 }
 
 // the value of lane l ^ S of the wave (S a power of two below 32)
@@ -843,6 +859,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int lsc = lead ? lane / h.g : OOB_OFFSET;
     const int lmc = (h.mg && lane % h.mg == 0) ? lane / h.mg : OOB_OFFSET;
     const float gts = (FP8S && h.nvfp4 && !AMAX) ? *p.tensor_scale : 1.0f;
+    const float rgts = 1.0f / gts;
+    // the statistics read zero dequantized values off the codes unless an NVFP4
+    // tensor scale is small enough for a nonzero code's value to underflow to 0
+    // (the smallest nonzero one is 0.5 x 2^-9 x g)
+    const bool codes_decide = !(FP8S && h.nvfp4) || gts >= 0x1p-100f;
     uint32_t tmax = 0;                     // AMAX: finite maximum of |x| as float bits
     double s2d = 0.0, e2d = 0.0;
     uint32_t nz = 0, fl = 0, zb = 0;
@@ -942,12 +963,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 cw = enc_fp4<EPC / 2>(y, scale);
                 if (nonfinite) cw = 0;
                 dec_fp4<EPC / 2>(cw, scale, d);
+                if (h.mg) {
 #pragma unroll
-                for (int i = 0; i < EPC; i++) d[i] = d[i] * sM;
+                    for (int i = 0; i < EPC; i++) d[i] = d[i] * sM;
+                }
                 if (nonfinite) code = 0xffu;
             } else {
-                float tt = __uint_as_float(am) / 6.0f;
-                if (h.nvfp4) tt = tt / gts;
+                // RN(1/6) = 0x3e2aaaab
+                float tt = div_lane(__uint_as_float(am), 6.0f, __uint_as_float(0x3e2aaaabu));
+                if (h.nvfp4) tt = div_lane(tt, gts, rgts);
                 const int sc = fp8_code(h.ue5 != 0, tt);
                 const float sb = fp8_value(h.ue5 != 0, sc);
                 const float S = h.nvfp4 ? sb * gts : sb;
@@ -960,9 +984,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
                     for (int i = 0; i < EPC; i++) v[i] = div_by(y[i], S, rS);
                 }
+                if (__any(S == 0.f)) {
 #pragma unroll
-                for (int i = 0; i < EPC; i++)
-                    if (S == 0.f) v[i] = (__float_as_uint(y[i]) >> 31) ? -0.f : 0.f;
+                    for (int i = 0; i < EPC; i++)
+                        if (S == 0.f) v[i] = (__float_as_uint(y[i]) >> 31) ? -0.f : 0.f;
+                }
                 cw = enc_fp4<EPC / 2>(v, 1.0f);
                 if (nonfinite) cw = 0;
                 dec_fp4<EPC / 2>(cw, 1.0f, d);
@@ -973,24 +999,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 }
                 code = nonfinite ? (h.ue5 ? 0xffu : 0x7fu) : (uint32_t)sc;
             }
-            if (nonfinite) {
+            if (__any(nonfinite)) {
 #pragma unroll
-                for (int i = 0; i < EPC; i++) d[i] = __uint_as_float(0x7fc00000u);
+                for (int i = 0; i < EPC; i++)
+                    if (nonfinite) d[i] = __uint_as_float(0x7fc00000u);
             }
             if constexpr (BF) __builtin_amdgcn_raw_buffer_store_b32(cw, rc, lco + k * 64 * CB, 0, 0);
             else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)cw, rc, lco + k * 64 * CB, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs, lsc + k * (64 / h.g), 0, 0);
             if constexpr (ST) {
                 float s2c = 0.f, e2c = 0.f;
-                uint32_t nzl = 0;
+                uint32_t nzl = 0, zin = 0;
 #pragma unroll
                 for (int i = 0; i < EPC; i++) {
                     const float ri = x[i] - d[i];
                     s2c = __builtin_fmaf(x[i], x[i], s2c);
                     e2c = __builtin_fmaf(ri, ri, e2c);
-                    nz += (x[i] != 0.f);
-                    fl += (x[i] != 0.f && d[i] == 0.f);
-                    nzl |= (d[i] != 0.f) ? 1u : 0u;    // NaN counts as non-zero
+                    zin += (x[i] == 0.f) ? 1u : 0u;
+                }
+                nz += EPC - zin;                       // NaN counts as non-zero
+                if (codes_decide) {
+                    // a dequantized value is zero exactly when its code's magnitude
+                    // is, and a zero input always gets such a code: flushed = zero
+                    // codes - zero inputs; a non-finite block (d NaN) flushes nothing
+                    // and is not all zero
+                    const uint32_t tm = cw & (BF ? 0x77777777u : 0x7777u);
+                    const uint32_t zc = __builtin_popcount(~(tm + (BF ? 0x77777777u : 0x7777u)) &
+                                                           (BF ? 0x88888888u : 0x8888u));
+                    fl += nonfinite ? 0u : zc - zin;
+                    nzl = (nonfinite || tm != 0u) ? 1u : 0u;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        fl += (x[i] != 0.f && d[i] == 0.f);
+                        nzl |= (d[i] != 0.f) ? 1u : 0u;
+                    }
                 }
                 if (fabsf(s2c) < INFINITY && fabsf(e2c) < INFINITY) {
                     s2d += (double)s2c;

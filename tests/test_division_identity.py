@@ -123,3 +123,38 @@ def test_random_nvfp4_divisors():
             g = np.float32(np.exp2(rng.uniform(-100, 60)))
             b = np.float32(ue4m3[rng.integers(0, len(ue4m3))] * g)
             _check(a_all[rng.integers(0, len(a_all), 50000)], b)
+
+
+def _fp32_sample(rng, n, lo_exp, hi_exp):
+    """random binary32 values with exponents uniform in [lo_exp, hi_exp) and random significands and signs"""
+    e = rng.integers(lo_exp + 127, hi_exp + 127, n).astype(np.uint32)
+    m = rng.integers(0, 1 << 23, n).astype(np.uint32)
+    s = rng.integers(0, 2, n).astype(np.uint32)
+    return ((s << 31) | (e << 23) | m).view(np.float32)
+
+
+def test_block_maxima_over_six():
+    """The NVFP4 / UE4M3 / UE5M3 block scale starts from amax / 6: the kernel
+    takes the same correction step with r = RN(1/6) for maxima in [2^-90,
+    2^120] (quotients in [2^-93, 2^118]); others divide exactly."""
+    rng = np.random.default_rng(11)
+    a = _bf16_inputs()
+    a = a[(np.abs(a) >= 2.0 ** -90) & (np.abs(a) <= 2.0 ** 120)]
+    _check(a, np.float32(6))
+    _check(np.abs(_fp32_sample(rng, 400000, -90, 120)), np.float32(6))
+
+
+def test_block_maxima_over_tensor_scales():
+    """NVFP4's amax / 6 is divided by the fp32 tensor scale g through r =
+    RN(1/g): the kernel takes that path when the dividend lies in [2^-90,
+    2^119] and RN(a r) in [2^-94, 2^118], which keeps the exact quotient
+    inside [2^-96, 2^120]; random g over 2^-126 .. 2^100."""
+    rng = np.random.default_rng(12)
+    for _ in range(60):
+        g = np.float32(np.exp2(rng.uniform(-126, 100)))
+        a = np.abs(_fp32_sample(rng, 20000, -90, 119))
+        with np.errstate(over="ignore", under="ignore"):
+            q0 = (a * (np.float32(1) / g)).astype(np.float32)
+        a = a[(q0 >= 2.0 ** -94) & (q0 <= 2.0 ** 118)]
+        if len(a):
+            _check(a, g)
