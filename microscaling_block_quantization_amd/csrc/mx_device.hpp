@@ -145,8 +145,25 @@ __device__ __forceinline__ float grid_value(const Elem& E, int idx) {
     }
 }
 
+// E2M1 code of v (already divided by its scale) under stochastic rounding,
+// from its bits.  Between neighbours lo <= |v| < hi the step is 2^(E-1) for
+// |v| = 2^E (1 + m 2^-23) in [1, 6) and 0.5 below 1, so (|v| - lo) / step * 2^16
+// is the bits below the code's mantissa bit over 64 ([1, 6)), the mantissa
+// over 128 ([0.5, 1)) or |v| 2^17 (below 0.5): go up iff r16 is below it.
+// |v| >= 6 (and Inf, NaN) takes the largest code.
+__device__ __forceinline__ int sr_e2m1(float v, uint32_t r16) {
+    const uint32_t b = fbits(v), u = b & 0x7fffffffu;
+    int idx;
+    if (u >= 0x40c00000u) idx = 7;
+    else if (u >= 0x3f800000u) idx = (int)((u >> 22) - 252u) + ((r16 << 6) < (u & 0x3fffffu) ? 1 : 0);
+    else if (u >= 0x3f000000u) idx = 1 + ((r16 << 7) < (u & 0x7fffffu) ? 1 : 0);
+    else idx = (float)r16 < bitsf(u) * 131072.0f ? 1 : 0;
+    return (int)((b >> 31) << 3) | idx;
+}
+
 // round v (already divided by its scale) to a code
 __device__ __forceinline__ int encode(const Elem& E, int mode, float v, uint32_t r16) {
+    if (E.kind == E2M1 && mode == SR) return sr_e2m1(v, r16);
     bool neg = (fbits(v) >> 31) != 0;
     float m = fabsf(v);
     if (E.kind == INT4 && E.asym && neg) m = 0.f;
