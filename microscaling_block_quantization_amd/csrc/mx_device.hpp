@@ -161,9 +161,14 @@ __device__ __forceinline__ int sr_e2m1(float v, uint32_t r16) {
     return (int)((b >> 31) << 3) | idx;
 }
 
-// round v (already divided by its scale) to a code
+// round v (already divided by its scale) to a code.  SR_BITS: E2M1 stochastic
+// rounding by sr_e2m1 (same codes as the grid search below; a kernel that
+// unrolls many elements and rarely takes that path keeps its code smaller
+// without it)
+template <bool SR_BITS = true>
 __device__ __forceinline__ int encode(const Elem& E, int mode, float v, uint32_t r16) {
-    if (E.kind == E2M1 && mode == SR) return sr_e2m1(v, r16);
+    if constexpr (SR_BITS)
+        if (E.kind == E2M1 && mode == SR) return sr_e2m1(v, r16);
     bool neg = (fbits(v) >> 31) != 0;
     float m = fabsf(v);
     if (E.kind == INT4 && E.asym && neg) m = 0.f;

@@ -350,7 +350,9 @@ __global__ __launch_bounds__(NT) void k_rows(QParams p, int amax_only) {
                 if (kind == 0) v = (p.asym ? (y[k] - o) : y[k]) * down;
                 else if (kind == 1) v = y[k] / S;
                 else v = (fbits(y[k]) >> 31) ? -0.f : 0.f;
-                c = encode(E, kind == 2 ? RTNE : p.round, v, rnd[k]);
+                // E2M1 rows with stochastic rounding and E8M0 scales take the
+                // wave-tile kernel unless a dequantized output is asked for
+                c = encode<false>(E, kind == 2 ? RTNE : p.round, v, rnd[k]);
                 float val = decode(E, c);
                 if (kind == 0) {
                     dv = val * up;
@@ -743,6 +745,7 @@ struct HwArgs {
     uint32_t fq;
     int ue5, nvfp4;          // fp8 scales: UE5M3, NVFP4 (UE4M3 times the tensor scale)
     float hconst;            // fp32 rounding of 1 / sqrt(h)
+    int sr;                  // E8M0 scales: stochastic rounding instead of to nearest
 };
 
 // a / b rounded to nearest even, given r = the correctly rounded 1 / b:
@@ -845,7 +848,9 @@ __device__ __forceinline__ uint32_t group_max_g(uint32_t v, int g) {
 
 // AMAX: the tensor pre-pass of NVFP4 scales instead: the finite maximum of
 // |x| (after the rotation) per workgroup into p.amax_parts
-template <bool BF, bool FP8S, bool ST, bool AMAX = false>
+// SRT: E8M0 scales with stochastic rounding (its own instantiation, so that
+// the Philox state does not weigh on the round-to-nearest kernels)
+template <bool BF, bool FP8S, bool ST, bool AMAX = false, bool SRT = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
     constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
@@ -960,7 +965,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 else sbits = (uint32_t)(fast_exp<false>(am, h.lq, h.fq) + 127) << 23;
                 code = sbits >> 23;
                 const float scale = __uint_as_float(sbits);
-                cw = enc_fp4<EPC / 2>(y, scale);
+                if constexpr (SRT) {
+                    // stochastic rounding of y 2^-e (e = code - 127, the general
+                    // kernel's single rounding): the draws of the chunk's elements,
+                    // 8 per Philox call at their linear indices (rows are dense)
+                    const uint64_t ch = (uint64_t)(t * TILE_CH + k * 64 + lane);
+                    uint32_t r[8];
+                    draws8(p.seed, p.off, BF ? ch : (ch >> 1), r);
+                    const float down = pow2f(127 - (int)code);
+                    cw = 0;
+#pragma unroll
+                    for (int i = 0; i < EPC; i++)
+                        cw |= (uint32_t)sr_e2m1(y[i] * down, BF ? r[i] : r[4 * (int)(ch & 1) + i]) << (4 * i);
+                } else {
+                    cw = enc_fp4<EPC / 2>(y, scale);
+                }
                 if (nonfinite) cw = 0;
                 dec_fp4<EPC / 2>(cw, scale, d);
                 if (h.mg) {
@@ -1143,10 +1162,12 @@ namespace {
 template <bool BF, bool FP8S>
 hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
-    auto k = st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>;
-    static int64_t cache[2] = {0, 0};   // one per statistics variant
+    const bool sr = !FP8S && h.sr;
+    auto k = sr ? (st ? k_rows_hw<BF, FP8S, true, false, !FP8S> : k_rows_hw<BF, FP8S, false, false, !FP8S>)
+                : (st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>);
+    static int64_t cache[4] = {0, 0, 0, 0};   // one per statistics and rounding variant
     int64_t g = fast_groups(p);
-    const int64_t r = resident(k, &cache[st ? 1 : 0]);
+    const int64_t r = resident(k, &cache[(st ? 1 : 0) + (sr ? 2 : 0)]);
     if (g > r) g = r;
     if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
     *grid = g;
@@ -1171,6 +1192,7 @@ void hw_args(const QParams& p, HwArgs& h) {
     h.fq = qb & 0x7fffffu;
     h.ue5 = p.scale == SC_UE5M3;
     h.nvfp4 = p.scale == SC_NVFP4;
+    h.sr = p.round == SR;
     const uint32_t hc = p.had == 16 ? 0x3E800000u : p.had == 32 ? 0x3E3504F3u : p.had == 64 ? 0x3E000000u : 0x3DB504F3u;
     memcpy(&h.hconst, &hc, 4);
 }
@@ -1180,7 +1202,8 @@ bool rows_hw_ok(const QParams& p) {
     const int epc = p.in_bf16 ? 8 : 4;
     const bool scale_ok = p.scale == SC_E8M0 || p.scale == SC_UE4M3 || p.scale == SC_UE5M3 || p.scale == SC_NVFP4;
     const int g = p.bc / epc;
-    return p.elem == E2M1 && p.round == RTNE && !p.asym && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
+    const bool round_ok = p.round == RTNE || (p.round == SR && p.scale == SC_E8M0);
+    return p.elem == E2M1 && round_ok && !p.asym && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
            g >= 1 && g <= 64 && g * epc == p.bc && (!p.had || p.had >= epc) && (!p.macro_cols || p.scale == SC_E8M0);
 }
 
