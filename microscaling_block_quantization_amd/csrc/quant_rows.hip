@@ -435,7 +435,7 @@ hipError_t launch_rows(const QParams& p, bool amax_only, hipStream_t s) {
     return hipGetLastError();
 }
 
-int64_t amax_grid(const QParams& p) { return rows_grid(p); }
+int64_t amax_grid(const QParams& p) { return std::max(rows_grid(p), rows_fast_grid(p)); }
 
 
 namespace {
@@ -1218,14 +1218,18 @@ hipError_t launch_rows_hw(const QParams& p, hipStream_t s, int64_t* grid) {
     return fp8s ? launch_hw_t<false, true>(p, h, s, grid) : launch_hw_t<false, false>(p, h, s, grid);
 }
 
-// The NVFP4 / E3M0 tensor pre-pass: on the wave-tile kernel (dense rows of a
-// format it takes), else on the general row kernel.  *grid: the partials written.
+// The NVFP4 / E3M0 tensor pre-pass (the finite maximum of |x|, after the
+// rotation when there is one): on the wave-tile kernel for a dense tensor of
+// whole 16-byte chunks per row (rotated only in the row formats it takes),
+// else on the general row kernel.  *grid: the partials written.
 hipError_t launch_amax(const QParams& p, hipStream_t s, int64_t* grid) {
     QParams a = p;
     a.dq = nullptr;
-    if (rows_hw_ok(a)) {
+    const int epc = a.in_bf16 ? 8 : 4;
+    if (a.ld == a.cols && a.cols % epc == 0 && (!a.had || rows_hw_ok(a))) {
         HwArgs h;
         hw_args(a, h);
+        if (h.g < 1) h.g = 1;   // the scale-block lanes are not used by the pre-pass
         auto k = a.in_bf16 ? k_rows_hw<true, true, false, true> : k_rows_hw<false, true, false, true>;
         static int64_t cache[2] = {0, 0};
         int64_t g = fast_groups(a);
