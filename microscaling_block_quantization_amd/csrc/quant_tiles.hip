@@ -28,6 +28,7 @@ using namespace mxd;
 namespace {
 
 constexpr int TROW = 1024;                     // bytes of one band row in LDS
+typedef float f2vr __attribute__((ext_vector_type(2)));
 
 // kinds of block scaling, in the LDS parameter word of a column
 enum { K_POW2 = 0, K_DIV = 1, K_ZERO = 2, K_NAN = 3 };
@@ -200,125 +201,178 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
     double s2 = 0, e2 = 0;
     unsigned long long nz = 0, fl = 0, zb = 0;
     const int64_t crow = code_row_bytes(E.bits, p.cols);
-#pragma unroll 1
-    for (int k = tid; k < NCH; k += NT) {
-        const int row = k >> 6, pc = k & 63;
-        const int cl = pc * EPC;                  // first column of the chunk in the tile
-        if (cl >= ncol) continue;
-        const int64_t r = r0 + row, c0 = col0 + cl;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + row * TROW + pc * 16);
-        uint32_t pr[EPC];
-#pragma unroll
-        for (int q = 0; q < EPC / 4; q++) {
-            const u32x4 t = *reinterpret_cast<const u32x4*>(prm + cl + 4 * q);
-            pr[4 * q] = t.x; pr[4 * q + 1] = t.y; pr[4 * q + 2] = t.z; pr[4 * q + 3] = t.w;
-        }
-        uint32_t rnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (p.round == SR) {
-            const uint64_t idx = (uint64_t)(r * p.cols + c0);
-            draws8(p.seed, p.off, idx >> 3, rnd);
-            if (!BF && (idx & 4)) {
-                rnd[0] = rnd[4]; rnd[1] = rnd[5]; rnd[2] = rnd[6]; rnd[3] = rnd[7];
-            }
-        }
-        int code[EPC];
-        float d[EPC], xs[EPC];
-        uint32_t nzmask = 0;
+    // Chunk k of the band is row k / 64, piece k % 64, and a thread visits k =
+    // tid, tid + NT, ...: always the same piece, so the same EPC columns.
+    // Their parameters are unpacked once: down = 2^-e and up = 2^e for a
+    // power-of-two scale (the divisor S and s_b for an fp8 one) and the offset.
+    const int pc = tid & 63, cl = pc * EPC;       // first column of the piece in the tile
+    if (cl < ncol) {
+        int kd[EPC], scd[EPC];
+        float dn[EPC], upv[EPC], of[EPC];
+        bool allpow2 = true;
 #pragma unroll
         for (int j = 0; j < EPC; j++) {
-            const float xv = BF ? word_elem<true>(w[j >> 1], j & 1) : __uint_as_float(w[j]);
-            const int sc = (int)(pr[j] & 0xff), kind = (int)((pr[j] >> 8) & 0xff);
-            int c;
-            float dv;
-            if (kind == K_NAN) {
-                c = 0;
-                dv = __uint_as_float(0x7fc00000u);
-            } else if (kind == K_POW2) {
-                const int e = p.scale == SC_E3M0 ? eref - sc : sc - 127;
-                const float o = bf16f((uint16_t)(pr[j] >> 16));
-                const float v = (p.asym ? (xv - o) : xv) * pow2f(-e);
-                c = encode(E, p.round, v, rnd[j]);
-                dv = decode(E, c) * pow2f(e);
-                if (p.asym) dv = dv + o;
+            const uint32_t pw = prm[cl + j];
+            scd[j] = (int)(pw & 0xff);
+            kd[j] = (int)((pw >> 8) & 0xff);
+            of[j] = bf16f((uint16_t)(pw >> 16));
+            if (kd[j] == K_POW2) {
+                const int e = p.scale == SC_E3M0 ? eref - scd[j] : scd[j] - 127;
+                dn[j] = pow2f(-e);
+                upv[j] = pow2f(e);
             } else {
-                const float sb = fp8_value(ue5, sc);
-                const float S = p.scale == SC_NVFP4 ? sb * g : sb;
-                const float v = kind == K_ZERO ? ((fbits(xv) >> 31) ? -0.f : 0.f) : xv / S;
-                c = encode(E, kind == K_ZERO ? RTNE : p.round, v, rnd[j]);
-                dv = decode(E, c) * sb;
-                if (p.scale == SC_NVFP4) dv = dv * g;
+                const float sb = fp8_value(ue5, scd[j]);
+                dn[j] = p.scale == SC_NVFP4 ? sb * g : sb;
+                upv[j] = sb;
             }
-            code[j] = c;
-            d[j] = dv;
-            xs[j] = xv;
-            nzmask |= (dv != 0.f ? 1u : 0u) << j;
+            allpow2 = allpow2 && kd[j] == K_POW2;
         }
-        if (nzmask) atomicAnd(&zmask[cl >> 5], ~(nzmask << (cl & 31)));
-        if (p.parts) {
-            float s2c = 0.f, e2c = 0.f;
-#pragma unroll
-            for (int j = 0; j < EPC; j++) {
-                const float rj = xs[j] - d[j];
-                s2c = __builtin_fmaf(xs[j], xs[j], s2c);
-                e2c = __builtin_fmaf(rj, rj, e2c);
-                nz += (xs[j] != 0.f);
-                fl += (xs[j] != 0.f && d[j] == 0.f);
-            }
-            if (fabsf(s2c) < INFINITY && fabsf(e2c) < INFINITY) {
-                s2 += (double)s2c;
-                e2 += (double)e2c;
-            } else {
-                // a square beyond the fp32 range (or a NaN): this chunk in float64
-#pragma unroll
-                for (int j = 0; j < EPC; j++) {
-                    const double xd = xs[j], dd = d[j];
-                    s2 += xd * xd;
-                    e2 += (xd - dd) * (xd - dd);
+        // E2M1 with power-of-two scales: to nearest by the pair convert on the
+        // scaled values (round to nearest even, saturating, signed zero kept),
+        // stochastically by sr_e2m1; then the pair decode, as the row kernels do
+        const bool hwc = E.kind == E2M1 && (p.round == RTNE || p.round == SR) && allpow2;
+#pragma unroll 1
+        for (int row = tid >> 6; row < BR; row += NT / 64) {
+            const int64_t r = r0 + row, c0 = col0 + cl;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + row * TROW + pc * 16);
+            uint32_t rnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (p.round == SR) {
+                const uint64_t idx = (uint64_t)(r * p.cols + c0);
+                draws8(p.seed, p.off, idx >> 3, rnd);
+                if (!BF && (idx & 4)) {
+                    rnd[0] = rnd[4]; rnd[1] = rnd[5]; rnd[2] = rnd[6]; rnd[3] = rnd[7];
                 }
             }
-        }
-        uint8_t* crw = p.codes + r * crow;
-        if (E.bits == 4) {
-            uint32_t word = 0;
+            int code[EPC];
+            float d[EPC], xs[EPC];
+            uint32_t nzmask = 0;
 #pragma unroll
-            for (int j = 0; j < EPC; j++) word |= (uint32_t)(code[j] & 0xf) << (4 * j);
-            if constexpr (BF) *reinterpret_cast<uint32_t*>(crw + c0 / 2) = word;
-            else *reinterpret_cast<uint16_t*>(crw + c0 / 2) = (uint16_t)word;
-        } else if (E.bits == 6) {
-            uint64_t bw = 0;
+            for (int j = 0; j < EPC; j++) xs[j] = BF ? word_elem<true>(w[j >> 1], j & 1) : __uint_as_float(w[j]);
+            if (hwc) {
+                float v[EPC];
 #pragma unroll
-            for (int j = 0; j < EPC; j++) bw |= (uint64_t)(code[j] & 0x3f) << (6 * j);
-            uint8_t* dst = crw + c0 * 3 / 4;
-            if constexpr (BF) {
-                uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
-                d16[0] = (uint16_t)bw; d16[1] = (uint16_t)(bw >> 16); d16[2] = (uint16_t)(bw >> 32);
+                for (int j = 0; j < EPC; j++) v[j] = (p.asym ? (xs[j] - of[j]) : xs[j]) * dn[j];
+                uint32_t cw = 0;
+                f2vr dq[EPC / 2];
+                if (p.round == SR) {
+#pragma unroll
+                    for (int j = 0; j < EPC; j++) cw |= (uint32_t)sr_e2m1(v[j], rnd[j]) << (4 * j);
+                } else {
+                    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[0], v[1], 1.0f, 0);
+                    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[2], v[3], 1.0f, 1);
+                    if constexpr (BF) {
+                        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[4], v[5], 1.0f, 2);
+                        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[6], v[7], 1.0f, 3);
+                    }
+                }
+                dq[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+                dq[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+                if constexpr (BF) {
+                    dq[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+                    dq[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+                }
+#pragma unroll
+                for (int q = 0; q < EPC / 2; q++) {
+                    d[2 * q] = dq[q][0] * upv[2 * q];
+                    d[2 * q + 1] = dq[q][1] * upv[2 * q + 1];
+                }
+#pragma unroll
+                for (int j = 0; j < EPC; j++) {
+                    if (p.asym) d[j] = d[j] + of[j];
+                    code[j] = (int)((cw >> (4 * j)) & 0xfu);
+                }
             } else {
-                dst[0] = (uint8_t)bw; dst[1] = (uint8_t)(bw >> 8); dst[2] = (uint8_t)(bw >> 16);
+#pragma unroll
+                for (int j = 0; j < EPC; j++) {
+                    int c;
+                    float dv;
+                    if (kd[j] == K_NAN) {
+                        c = 0;
+                        dv = __uint_as_float(0x7fc00000u);
+                    } else if (kd[j] == K_POW2) {
+                        const float v = (p.asym ? (xs[j] - of[j]) : xs[j]) * dn[j];
+                        c = encode(E, p.round, v, rnd[j]);
+                        dv = decode(E, c) * upv[j];
+                        if (p.asym) dv = dv + of[j];
+                    } else {
+                        const float v = kd[j] == K_ZERO ? ((fbits(xs[j]) >> 31) ? -0.f : 0.f) : xs[j] / dn[j];
+                        c = encode(E, kd[j] == K_ZERO ? RTNE : p.round, v, rnd[j]);
+                        dv = decode(E, c) * upv[j];
+                        if (p.scale == SC_NVFP4) dv = dv * g;
+                    }
+                    code[j] = c;
+                    d[j] = dv;
+                }
             }
-        } else {
-            uint32_t lo = 0, hi = 0;
 #pragma unroll
-            for (int j = 0; j < 4; j++) lo |= (uint32_t)(code[j] & 0xff) << (8 * j);
-            if constexpr (BF) {
+            for (int j = 0; j < EPC; j++) nzmask |= (d[j] != 0.f ? 1u : 0u) << j;
+            if (nzmask) atomicAnd(&zmask[cl >> 5], ~(nzmask << (cl & 31)));
+            if (p.parts) {
+                float s2c = 0.f, e2c = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; j++) hi |= (uint32_t)(code[4 + j] & 0xff) << (8 * j);
-                *reinterpret_cast<uint2*>(crw + c0) = make_uint2(lo, hi);
-            } else {
-                *reinterpret_cast<uint32_t*>(crw + c0) = lo;
+                for (int j = 0; j < EPC; j++) {
+                    const float rj = xs[j] - d[j];
+                    s2c = __builtin_fmaf(xs[j], xs[j], s2c);
+                    e2c = __builtin_fmaf(rj, rj, e2c);
+                    nz += (xs[j] != 0.f);
+                    fl += (xs[j] != 0.f && d[j] == 0.f);
+                }
+                if (fabsf(s2c) < INFINITY && fabsf(e2c) < INFINITY) {
+                    s2 += (double)s2c;
+                    e2 += (double)e2c;
+                } else {
+                    // a square beyond the fp32 range (or a NaN): this chunk in float64
+#pragma unroll
+                    for (int j = 0; j < EPC; j++) {
+                        const double xd = xs[j], dd = d[j];
+                        s2 += xd * xd;
+                        e2 += (xd - dd) * (xd - dd);
+                    }
+                }
             }
-        }
-        if (p.dq) {
-            if (p.dq_bf16) {
-                uint16_t* dst = static_cast<uint16_t*>(p.dq) + r * p.cols + c0;
-                uint32_t pk[EPC / 2];
+            uint8_t* crw = p.codes + r * crow;
+            if (E.bits == 4) {
+                uint32_t word = 0;
 #pragma unroll
-                for (int j = 0; j < EPC / 2; j++) pk[j] = bf16_rne(d[2 * j]) | ((uint32_t)bf16_rne(d[2 * j + 1]) << 16);
-                if constexpr (BF) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+                for (int j = 0; j < EPC; j++) word |= (uint32_t)(code[j] & 0xf) << (4 * j);
+                if constexpr (BF) *reinterpret_cast<uint32_t*>(crw + c0 / 2) = word;
+                else *reinterpret_cast<uint16_t*>(crw + c0 / 2) = (uint16_t)word;
+            } else if (E.bits == 6) {
+                uint64_t bw = 0;
+#pragma unroll
+                for (int j = 0; j < EPC; j++) bw |= (uint64_t)(code[j] & 0x3f) << (6 * j);
+                uint8_t* dst = crw + c0 * 3 / 4;
+                if constexpr (BF) {
+                    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+                    d16[0] = (uint16_t)bw; d16[1] = (uint16_t)(bw >> 16); d16[2] = (uint16_t)(bw >> 32);
+                } else {
+                    dst[0] = (uint8_t)bw; dst[1] = (uint8_t)(bw >> 8); dst[2] = (uint8_t)(bw >> 16);
+                }
             } else {
-                float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.dq) + r * p.cols + c0);
-                dst[0] = make_float4(d[0], d[1], d[2], d[3]);
-                if constexpr (BF) dst[1] = make_float4(d[4], d[5], d[6], d[7]);
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < 4; j++) lo |= (uint32_t)(code[j] & 0xff) << (8 * j);
+                if constexpr (BF) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) hi |= (uint32_t)(code[4 + j] & 0xff) << (8 * j);
+                    *reinterpret_cast<uint2*>(crw + c0) = make_uint2(lo, hi);
+                } else {
+                    *reinterpret_cast<uint32_t*>(crw + c0) = lo;
+                }
+            }
+            if (p.dq) {
+                if (p.dq_bf16) {
+                    uint16_t* dst = static_cast<uint16_t*>(p.dq) + r * p.cols + c0;
+                    uint32_t pk[EPC / 2];
+#pragma unroll
+                    for (int j = 0; j < EPC / 2; j++) pk[j] = bf16_rne(d[2 * j]) | ((uint32_t)bf16_rne(d[2 * j + 1]) << 16);
+                    if constexpr (BF) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+                } else {
+                    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.dq) + r * p.cols + c0);
+                    dst[0] = make_float4(d[0], d[1], d[2], d[3]);
+                    if constexpr (BF) dst[1] = make_float4(d[4], d[5], d[6], d[7]);
+                }
             }
         }
     }
