@@ -231,6 +231,11 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
         // scaled values (round to nearest even, saturating, signed zero kept),
         // stochastically by sr_e2m1; then the pair decode, as the row kernels do
         const bool hwc = E.kind == E2M1 && (p.round == RTNE || p.round == SR) && allpow2;
+        // INT4 to nearest with power-of-two scales: the integer nearest |v|
+        // (ties to even), capped at the largest code; the unsigned variant
+        // takes a negative v as zero, the signed one keeps the sign in two's
+        // complement (the general encode and decode, written out)
+        const bool i4 = E.kind == INT4 && p.round == RTNE && allpow2;
 #pragma unroll 1
         for (int row = tid >> 6; row < BR; row += NT / 64) {
             const int64_t r = r0 + row, c0 = col0 + cl;
@@ -280,6 +285,19 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                 for (int j = 0; j < EPC; j++) {
                     if (p.asym) d[j] = d[j] + of[j];
                     code[j] = (int)((cw >> (4 * j)) & 0xfu);
+                }
+            } else if (i4) {
+                const float qcap = (float)E.maxidx;
+#pragma unroll
+                for (int j = 0; j < EPC; j++) {
+                    const float v = (p.asym ? (xs[j] - of[j]) : xs[j]) * dn[j];
+                    const bool neg = (fbits(v) >> 31) != 0;
+                    const float m = (p.asym && neg) ? 0.f : fabsf(v);
+                    const int idx = (int)fminf(rintf(m), qcap);
+                    const int sv = (!p.asym && neg) ? -idx : idx;
+                    code[j] = p.asym ? idx : (sv & 0xf);
+                    d[j] = (float)sv * upv[j];
+                    if (p.asym) d[j] = d[j] + of[j];
                 }
             } else {
 #pragma unroll
