@@ -746,6 +746,7 @@ struct HwArgs {
     int ue5, nvfp4;          // fp8 scales: UE5M3, NVFP4 (UE4M3 times the tensor scale)
     float hconst;            // fp32 rounding of 1 / sqrt(h)
     int sr;                  // E8M0 scales: stochastic rounding instead of to nearest
+    int e3m0;                // E3M0 scales: a step-down below the tensor's reference exponent
 };
 
 // a / b rounded to nearest even, given r = the correctly rounded 1 / b:
@@ -848,9 +849,10 @@ __device__ __forceinline__ uint32_t group_max_g(uint32_t v, int g) {
 
 // AMAX: the tensor pre-pass of NVFP4 scales instead: the finite maximum of
 // |x| (after the rotation) per workgroup into p.amax_parts
-// SRT: E8M0 scales with stochastic rounding (its own instantiation, so that
-// the Philox state does not weigh on the round-to-nearest kernels)
-template <bool BF, bool FP8S, bool ST, bool AMAX = false, bool SRT = false>
+// MODE (power-of-two scales, FP8S false): 0 E8M0 to nearest, 1 E8M0 with
+// stochastic rounding, 2 E3M0 to nearest.  Each has its own instantiation, so
+// that the Philox state or the E3M0 logic does not weigh on the others.
+template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
     constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
@@ -864,6 +866,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int lsc = lead ? lane / h.g : OOB_OFFSET;
     const int lmc = (h.mg && lane % h.mg == 0) ? lane / h.mg : OOB_OFFSET;
     const float gts = (FP8S && h.nvfp4 && !AMAX) ? *p.tensor_scale : 1.0f;
+    const int eref = (!FP8S && !AMAX && MODE == 2) ? *p.ref_exp : 0;
     const float rgts = 1.0f / gts;
     // the statistics read zero dequantized values off the codes unless an NVFP4
     // tensor scale is small enough for a nonzero code's value to underflow to 0
@@ -960,12 +963,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
             uint32_t cw = 0, code;
             float d[EPC];
             if constexpr (!FP8S) {
+              if constexpr (MODE == 2) {
+                // E3M0: step-down c = e_ref - e_ceil(amax, 6) clamped to 0 .. 7 (7
+                // for an all-zero block), scale 2^(e_ref - c); the elements scaled,
+                // rounded by the pair convert and decoded with 2^e as the general
+                // row kernel does
+                int cd = 7;
+                if (am != 0u && !nonfinite) {
+                    cd = eref - e_ceil(__uint_as_float(am), 6.0f);
+                    cd = cd < 0 ? 0 : (cd > 7 ? 7 : cd);
+                }
+                const int e = eref - cd;
+                const float down = pow2f(-e), up = pow2f(e);
+                float v[EPC];
+#pragma unroll
+                for (int i = 0; i < EPC; i++) v[i] = y[i] * down;
+                cw = enc_fp4<EPC / 2>(v, 1.0f);
+                if (nonfinite) cw = 0;
+                dec_fp4<EPC / 2>(cw, up, d);
+                code = nonfinite ? 0xffu : (uint32_t)cd;
+              } else {
                 uint32_t sbits;
                 if (h.floor_rule) sbits = __builtin_elementwise_sub_sat(am & 0x7f800000u, 0x01000000u);
                 else sbits = (uint32_t)(fast_exp<false>(am, h.lq, h.fq) + 127) << 23;
                 code = sbits >> 23;
                 const float scale = __uint_as_float(sbits);
-                if constexpr (SRT) {
+                if constexpr (MODE == 1) {
                     // stochastic rounding of y 2^-e (e = code - 127, the general
                     // kernel's single rounding): the draws of the chunk's elements,
                     // 8 per Philox call at their linear indices (rows are dense)
@@ -987,6 +1010,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                     for (int i = 0; i < EPC; i++) d[i] = d[i] * sM;
                 }
                 if (nonfinite) code = 0xffu;
+              }
             } else {
                 // RN(1/6) = 0x3e2aaaab
                 float tt = div_lane(__uint_as_float(am), 6.0f, __uint_as_float(0x3e2aaaabu));
@@ -1162,12 +1186,14 @@ namespace {
 template <bool BF, bool FP8S>
 hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
-    const bool sr = !FP8S && h.sr;
-    auto k = sr ? (st ? k_rows_hw<BF, FP8S, true, false, !FP8S> : k_rows_hw<BF, FP8S, false, false, !FP8S>)
-                : (st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>);
-    static int64_t cache[4] = {0, 0, 0, 0};   // one per statistics and rounding variant
+    constexpr int M1 = FP8S ? 0 : 1, M2 = FP8S ? 0 : 2;
+    const int mode = FP8S ? 0 : (h.sr ? 1 : (h.e3m0 ? 2 : 0));
+    auto k = mode == 1 ? (st ? k_rows_hw<BF, FP8S, true, false, M1> : k_rows_hw<BF, FP8S, false, false, M1>)
+           : mode == 2 ? (st ? k_rows_hw<BF, FP8S, true, false, M2> : k_rows_hw<BF, FP8S, false, false, M2>)
+                       : (st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>);
+    static int64_t cache[6] = {0, 0, 0, 0, 0, 0};   // one per statistics and mode variant
     int64_t g = fast_groups(p);
-    const int64_t r = resident(k, &cache[(st ? 1 : 0) + (sr ? 2 : 0)]);
+    const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode]);
     if (g > r) g = r;
     if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
     *grid = g;
@@ -1193,6 +1219,7 @@ void hw_args(const QParams& p, HwArgs& h) {
     h.ue5 = p.scale == SC_UE5M3;
     h.nvfp4 = p.scale == SC_NVFP4;
     h.sr = p.round == SR;
+    h.e3m0 = p.scale == SC_E3M0;
     const uint32_t hc = p.had == 16 ? 0x3E800000u : p.had == 32 ? 0x3E3504F3u : p.had == 64 ? 0x3E000000u : 0x3DB504F3u;
     memcpy(&h.hconst, &hc, 4);
 }
@@ -1200,7 +1227,8 @@ void hw_args(const QParams& p, HwArgs& h) {
 
 bool rows_hw_ok(const QParams& p) {
     const int epc = p.in_bf16 ? 8 : 4;
-    const bool scale_ok = p.scale == SC_E8M0 || p.scale == SC_UE4M3 || p.scale == SC_UE5M3 || p.scale == SC_NVFP4;
+    const bool scale_ok = p.scale == SC_E8M0 || p.scale == SC_UE4M3 || p.scale == SC_UE5M3 || p.scale == SC_NVFP4 ||
+                          p.scale == SC_E3M0;
     const int g = p.bc / epc;
     const bool round_ok = p.round == RTNE || (p.round == SR && p.scale == SC_E8M0);
     return p.elem == E2M1 && round_ok && !p.asym && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
@@ -1213,7 +1241,7 @@ hipError_t launch_rows_hw(const QParams& p, hipStream_t s, int64_t* grid) {
     *grid = 0;
     HwArgs h;
     hw_args(p, h);
-    const bool fp8s = p.scale != SC_E8M0;
+    const bool fp8s = p.scale == SC_UE4M3 || p.scale == SC_UE5M3 || p.scale == SC_NVFP4;
     if (p.in_bf16) return fp8s ? launch_hw_t<true, true>(p, h, s, grid) : launch_hw_t<true, false>(p, h, s, grid);
     return fp8s ? launch_hw_t<false, true>(p, h, s, grid) : launch_hw_t<false, false>(p, h, s, grid);
 }
