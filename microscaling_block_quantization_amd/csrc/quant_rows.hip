@@ -747,6 +747,7 @@ struct HwArgs {
     float hconst;            // fp32 rounding of 1 / sqrt(h)
     int sr;                  // E8M0 scales: stochastic rounding instead of to nearest
     int e3m0;                // E3M0 scales: a step-down below the tensor's reference exponent
+    int int4, asym;          // INT4 elements (E8M0 scales, to nearest), the min/max variant
 };
 
 // a / b rounded to nearest even, given r = the correctly rounded 1 / b:
@@ -847,11 +848,26 @@ __device__ __forceinline__ uint32_t group_max_g(uint32_t v, int g) {
     return v;
 }
 
+// the minimum (MAXV false) or maximum of a float over aligned groups of g
+// lanes, by the lane moves of group_max_g
+template <bool MAXV>
+__device__ __forceinline__ float group_fext_g(float v, int g) {
+    auto op = [](float a, uint32_t b) { return MAXV ? fmaxf(a, __uint_as_float(b)) : fminf(a, __uint_as_float(b)); };
+    if (g >= 2) v = op(v, dpp<DPP_XOR1>(__float_as_uint(v)));
+    if (g >= 4) v = op(v, dpp<DPP_XOR2>(__float_as_uint(v)));
+    if (g >= 8) v = op(v, dpp<DPP_HALF_MIRROR>(__float_as_uint(v)));
+    if (g >= 16) v = op(v, dpp<DPP_ROW_MIRROR>(__float_as_uint(v)));
+    if (g >= 32) v = op(v, (uint32_t)__shfl_xor((int)__float_as_uint(v), 16, 64));
+    if (g >= 64) v = op(v, (uint32_t)__shfl_xor((int)__float_as_uint(v), 32, 64));
+    return v;
+}
+
 // AMAX: the tensor pre-pass of NVFP4 scales instead: the finite maximum of
 // |x| (after the rotation) per workgroup into p.amax_parts
 // MODE (power-of-two scales, FP8S false): 0 E8M0 to nearest, 1 E8M0 with
-// stochastic rounding, 2 E3M0 to nearest.  Each has its own instantiation, so
-// that the Philox state or the E3M0 logic does not weigh on the others.
+// stochastic rounding, 2 E3M0 to nearest, 3 INT4 elements with E8M0 scales to
+// nearest (plain or min/max).  Each has its own instantiation, so that the
+// Philox state or the other modes' logic does not weigh on the rest.
 template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
     constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
@@ -865,13 +881,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const bool lead = lane % h.g == 0;
     const int lsc = lead ? lane / h.g : OOB_OFFSET;
     const int lmc = (h.mg && lane % h.mg == 0) ? lane / h.mg : OOB_OFFSET;
+    const int lof = lead ? (lane / h.g) * 2 : OOB_OFFSET;   // INT4 min/max: bf16 offset bytes
     const float gts = (FP8S && h.nvfp4 && !AMAX) ? *p.tensor_scale : 1.0f;
     const int eref = (!FP8S && !AMAX && MODE == 2) ? *p.ref_exp : 0;
     const float rgts = 1.0f / gts;
     // the statistics read zero dequantized values off the codes unless an NVFP4
     // tensor scale is small enough for a nonzero code's value to underflow to 0
     // (the smallest nonzero one is 0.5 x 2^-9 x g)
-    const bool codes_decide = !(FP8S && h.nvfp4) || gts >= 0x1p-100f;
+    const bool codes_decide = MODE != 3 && (!(FP8S && h.nvfp4) || gts >= 0x1p-100f);
     uint32_t tmax = 0;                     // AMAX: finite maximum of |x| as float bits
     double s2d = 0.0, e2d = 0.0;
     uint32_t nz = 0, fl = 0, zb = 0;
@@ -886,6 +903,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         const rsrc_t rc = buf(p.codes + t * TILE_CH * CB, nv * CB);
         const rsrc_t rs = buf(p.scales + t * (TILE_CH / h.g), nv / h.g);
         const rsrc_t rm = buf(h.mg ? p.macro + t * (TILE_CH / (h.mg ? h.mg : 1)) : p.codes, h.mg ? nv / h.mg : 0);
+        const rsrc_t ro = buf(MODE == 3 && h.asym ? (const void*)(p.offsets + t * (TILE_CH / h.g)) : (const void*)p.codes,
+                              MODE == 3 && h.asym ? (nv / h.g) * 2 : 0);
         u32x4 w[FAST_NL];
 #pragma unroll
         for (int k = 0; k < FAST_NL; k++)
@@ -963,7 +982,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
             uint32_t cw = 0, code;
             float d[EPC];
             if constexpr (!FP8S) {
-              if constexpr (MODE == 2) {
+              if constexpr (MODE == 3) {
+                // INT4, E8M0 scale 2^e, to nearest.  Min/max variant: offset o =
+                // bf16 floor of the block minimum, e from the range max - o, codes
+                // 0 .. 15 of (x - o) 2^-e (a negative value takes 0); plain: e
+                // from max |x|, codes -7 .. 7 in two's complement.  The integer
+                // nearest |v| ties to even and is capped at the largest code.
+                const Elem E4 = make_elem(INT4, h.asym);
+                float lo = y[0], hi = y[0];
+#pragma unroll
+                for (int i = 1; i < EPC; i++) { lo = fminf(lo, y[i]); hi = fmaxf(hi, y[i]); }
+                int e;
+                uint16_t ob = 0;
+                float o = 0.f;
+                if (h.asym) {
+                    lo = group_fext_g<false>(lo, h.g);
+                    hi = group_fext_g<true>(hi, h.g);
+                    ob = bf16_floor(lo);
+                    o = bf16f(ob);
+                    const float R = hi - o;
+                    e = R > 0.f ? e8m0_exp(p.rule, p.tau, E4, R) : -127;
+                } else {
+                    e = e8m0_exp(p.rule, p.tau, E4, __uint_as_float(am));
+                }
+                const float down = pow2f(-e), up = pow2f(e), qcap = (float)E4.maxidx;
+                cw = 0;
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    const float v = (h.asym ? (y[i] - o) : y[i]) * down;
+                    const bool neg = (__float_as_uint(v) >> 31) != 0;
+                    const float m = (h.asym && neg) ? 0.f : fabsf(v);
+                    const int idx = (int)fminf(rintf(m), qcap);
+                    const int sv = (!h.asym && neg) ? -idx : idx;
+                    cw |= (uint32_t)(h.asym ? idx : (sv & 0xf)) << (4 * i);
+                    d[i] = (float)sv * up;
+                    if (h.asym) d[i] = d[i] + o;
+                }
+                if (nonfinite) cw = 0;
+                code = nonfinite ? 0xffu : (uint32_t)(e + 127);
+                if (h.asym)
+                    __builtin_amdgcn_raw_buffer_store_b16(nonfinite ? (uint16_t)0 : ob, ro, lof + k * (64 / h.g) * 2, 0, 0);
+              } else if constexpr (MODE == 2) {
                 // E3M0: step-down c = e_ref - e_ceil(amax, 6) clamped to 0 .. 7 (7
                 // for an all-zero block), scale 2^(e_ref - c); the elements scaled,
                 // rounded by the pair convert and decoded with 2^e as the general
@@ -1186,12 +1245,13 @@ namespace {
 template <bool BF, bool FP8S>
 hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
-    constexpr int M1 = FP8S ? 0 : 1, M2 = FP8S ? 0 : 2;
-    const int mode = FP8S ? 0 : (h.sr ? 1 : (h.e3m0 ? 2 : 0));
+    constexpr int M1 = FP8S ? 0 : 1, M2 = FP8S ? 0 : 2, M3 = FP8S ? 0 : 3;
+    const int mode = FP8S ? 0 : (h.int4 ? 3 : (h.sr ? 1 : (h.e3m0 ? 2 : 0)));
     auto k = mode == 1 ? (st ? k_rows_hw<BF, FP8S, true, false, M1> : k_rows_hw<BF, FP8S, false, false, M1>)
            : mode == 2 ? (st ? k_rows_hw<BF, FP8S, true, false, M2> : k_rows_hw<BF, FP8S, false, false, M2>)
+           : mode == 3 ? (st ? k_rows_hw<BF, FP8S, true, false, M3> : k_rows_hw<BF, FP8S, false, false, M3>)
                        : (st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>);
-    static int64_t cache[6] = {0, 0, 0, 0, 0, 0};   // one per statistics and mode variant
+    static int64_t cache[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // one per statistics and mode variant
     int64_t g = fast_groups(p);
     const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode]);
     if (g > r) g = r;
@@ -1220,6 +1280,8 @@ void hw_args(const QParams& p, HwArgs& h) {
     h.nvfp4 = p.scale == SC_NVFP4;
     h.sr = p.round == SR;
     h.e3m0 = p.scale == SC_E3M0;
+    h.int4 = p.elem == INT4;
+    h.asym = p.asym;
     const uint32_t hc = p.had == 16 ? 0x3E800000u : p.had == 32 ? 0x3E3504F3u : p.had == 64 ? 0x3E000000u : 0x3DB504F3u;
     memcpy(&h.hconst, &hc, 4);
 }
@@ -1231,7 +1293,9 @@ bool rows_hw_ok(const QParams& p) {
                           p.scale == SC_E3M0;
     const int g = p.bc / epc;
     const bool round_ok = p.round == RTNE || (p.round == SR && p.scale == SC_E8M0);
-    return p.elem == E2M1 && round_ok && !p.asym && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
+    const bool elem_ok = (p.elem == E2M1 && !p.asym) ||
+                         (p.elem == INT4 && p.round == RTNE && p.scale == SC_E8M0 && !p.macro_cols);
+    return elem_ok && round_ok && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
            g >= 1 && g <= 64 && g * epc == p.bc && (!p.had || p.had >= epc) && (!p.macro_cols || p.scale == SC_E8M0);
 }
 

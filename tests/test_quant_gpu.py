@@ -72,7 +72,8 @@ W4_FORMATS = [dict(), dict(hadamard=32), dict(hadamard=128), dict(block_cols=16)
               dict(macro_cols=128, block_cols=32, rule=FLOOR),
               dict(scale=NVFP4, block_cols=16), dict(scale=NVFP4, block_cols=16, hadamard=16),
               dict(scale=NVFP4, block_cols=16, hadamard=32), dict(hadamard=64, rule=OAS, oas_tau=7.5),
-              dict(hadamard=32, round=SR, seed=17), dict(macro_cols=128, block_cols=16, rule=CEIL, round=SR, seed=19)]
+              dict(hadamard=32, round=SR, seed=17), dict(macro_cols=128, block_cols=16, rule=CEIL, round=SR, seed=19),
+              dict(elem=INT4, hadamard=32)]
 
 
 @pytest.mark.parametrize("kw", W4_FORMATS, ids=kid)
