@@ -718,11 +718,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
 }
 
 // ---------------------------------------------------------------------------
-// Hardware-convert row kernel for the other E2M1 round-to-nearest formats:
-// UE4M3 / UE5M3 / NVFP4 block scales, block Hadamard rotation ("Bridging the
-// Gap ... Microscaling FP4 Quantization", Sec. 2.2) and macro-block scaling
-// ("Unveiling the Potential of Quantization with MXFP4", Sec. 4), with E8M0
-// or fp8 block scales; dense rows, no dequantized output.  Wave tile, buffer
+// Wave-tile row kernel for the other dense row formats: E2M1 under UE4M3 /
+// UE5M3 / NVFP4, E8M0 or E3M0 block scales, with block Hadamard rotation
+// ("Bridging the Gap ... Microscaling FP4 Quantization", Sec. 2.2) or
+// macro-block scaling ("Unveiling the Potential of Quantization with MXFP4",
+// Sec. 4), to nearest or (E8M0 scales) stochastically; INT4, plain or min/max,
+// under E8M0 scales to nearest (the ARITH 2025 MX-training report's
+// asymmetric INT4).  Dense rows, no dequantized output.  Wave tile, buffer
 // I/O and grid-stride loop as in k_rows_fast; the lane groups (scale block: g
 // lanes, rotation chunk: hg, macro block: mg) are uniform run-time sizes.
 //  - rotation: the butterflies of a chunk's EPC elements in registers, then
@@ -735,7 +737,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
 //  - E8M0 scales: the scaled FP4 convert divides by the power of two itself
 //    (it reads the exponent field of the scale operand); fp8 scales: the
 //    elements are divided by S (correctly rounded) and converted unscaled;
-//  - decode by the matching FP4 -> f32 convert, times s_b (and g) or s_M.
+//    E3M0 scales: the elements times 2^-e, converted unscaled;
+//  - stochastic rounding: one Philox call per 8 elements at their linear
+//    indices, the E2M1 code decided from the bits of the scaled value;
+//  - INT4: the integer nearest the scaled value (ties to even), capped; the
+//    min/max variant subtracts the bf16 offset first and stores it per block;
+//  - decode by the matching FP4 -> f32 convert, times s_b (and g) or s_M
+//    (INT4: the integer times 2^e, plus the offset).
 // ---------------------------------------------------------------------------
 struct HwArgs {
     int64_t nchunks;
