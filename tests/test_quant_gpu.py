@@ -252,6 +252,17 @@ def test_w3_full_size_sr():
     check_quantize(x, dict(round=SR, seed=synth.SR_SEED, block_rows=32, block_cols=32), "w3 full SR 2D")
 
 
+# the gradient cells whose rows take the wave-tile kernel, and column blocks of the others
+@pytest.mark.slow
+@pytest.mark.parametrize("kw", [dict(round=SR, seed=synth.SR_SEED), dict(scale=SE3M0, rule=CEIL),
+                                dict(elem=INT4, asymmetric=1, rule=CEIL),
+                                dict(scale=SE3M0, rule=CEIL, block_rows=32, block_cols=1),
+                                dict(elem=INT4, asymmetric=1, rule=CEIL, block_rows=32, block_cols=1)], ids=kid)
+def test_w3_full_size_cells(kw):
+    x = synth.w3()
+    check_quantize(x, kw, f"w3 full {kid(kw)}")
+
+
 @pytest.mark.slow
 def test_w4_full_size_h128():
     x = synth.w4()
