@@ -20,6 +20,7 @@
 // flight in the loop are the DMA the stage waits count (and, with macro-block
 // scales, one byte per operand row a stage ahead).
 #include "mx_kernels.hpp"
+#include "gemm_cstore.hpp"
 
 namespace mxk {
 using namespace mxd;
@@ -440,20 +441,26 @@ __global__ __launch_bounds__(64 * G::NW) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     wait_vm<0>();
 
+    if constexpr (CBF16) {
+        // bf16 C through a private 16-row strip of each wave in the ring (free
+        // once every wave has read the last stage), then 16-byte row stores
+        static_assert(G::NW * CStore<G>::AREA <= G::D * G::STAGE, "C strips fit in the ring");
+        __syncthreads();
+        store_c_bf16<G, false>(acc, smem + wave * CStore<G>::AREA, C, m0, n0, M, N, ldc, wm, wn, lane, half, lrow);
+    } else {
 #pragma unroll
-    for (int i = 0; i < TI; i++)
+        for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < TJ; j++) {
-            const int64_t n = n0 + wn * 32 * TJ + 32 * j + lrow;
-            if (n >= N) continue;
+            for (int j = 0; j < TJ; j++) {
+                const int64_t n = n0 + wn * 32 * TJ + 32 * j + lrow;
+                if (n >= N) continue;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + wm * 32 * TI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
-                if (m >= M) continue;
-                if constexpr (CBF16) static_cast<uint16_t*>(C)[m * ldc + n] = bf16_rne(acc[i][j][r]);
-                else static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
+                for (int r = 0; r < 16; r++) {
+                    const int64_t m = m0 + wm * 32 * TI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
+                    if (m < M) static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
+                }
             }
-        }
+    }
 }
 
 #ifndef LDS_WGM
