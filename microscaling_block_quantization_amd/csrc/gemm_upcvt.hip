@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "mx_kernels.hpp"
+#include "gemm_cstore.hpp"
 
 namespace mxk {
 using namespace mxd;
@@ -402,6 +403,11 @@ __device__ __forceinline__ void ustep(uint8_t* smem, const UPanels& P, int s, in
     }
 }
 
+// the wave tiles of k_gemm_upcvt_lds as the shared C store path sees them
+struct UCGeo {
+    static constexpr int TI = UTI, TJ = UTJ, BM = UBM;
+};
+
 template <bool CBF16, int KA, int KB>
 __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_upcvt_lds(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
@@ -473,18 +479,29 @@ __global__ __launch_bounds__(64 * UNW) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int i = 0; i < UTI; i++)
 #pragma unroll
-        for (int j = 0; j < UTJ; j++) {
-            const int64_t n = n0 + wn * 32 * UTJ + 32 * j + lrow;
-            if (n >= N) continue;
+        for (int j = 0; j < UTJ; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + wm * 32 * UTI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
-                if (m >= M) continue;
-                const float v = acc[i][j][r] * g;
-                if constexpr (CBF16) static_cast<uint16_t*>(C)[m * ldc + n] = bf16_rne(v);
-                else static_cast<float*>(C)[m * ldc + n] = v;
+            for (int r = 0; r < 16; r++) acc[i][j][r] = acc[i][j][r] * g;
+    if constexpr (CBF16) {
+        // bf16 C through a private 16-row strip of each wave in the ring (free
+        // once every wave has read the last stage), then 16-byte row stores
+        static_assert(UNW * CStore<UCGeo>::AREA <= UD * USTAGE, "C strips fit in the ring");
+        __syncthreads();
+        store_c_bf16<UCGeo, false>(acc, smem + wave * CStore<UCGeo>::AREA, C, m0, n0, M, N, ldc, wm, wn, lane, half, lrow);
+    } else {
+#pragma unroll
+        for (int i = 0; i < UTI; i++)
+#pragma unroll
+            for (int j = 0; j < UTJ; j++) {
+                const int64_t n = n0 + wn * 32 * UTJ + 32 * j + lrow;
+                if (n >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int64_t m = m0 + wm * 32 * UTI + 32 * i + 8 * (r / 4) + 4 * half + (r % 4);
+                    if (m < M) static_cast<float*>(C)[m * ldc + n] = acc[i][j][r];
+                }
             }
-        }
+    }
 }
 
 UDec udec(const UOperand& U) {
