@@ -4,6 +4,8 @@
 One step = one W4A4 linear layer at Llama-8B MLP shape, on synthetic data:
   quantize A (bf16 8192 x 4096 ~ N(0, 1))      -> MXFP4 codes + E8M0 scales + stats
   quantize B (bf16 14336 x 4096 ~ N(0, .02^2)) -> MXFP4 codes + E8M0 scales + stats
+    (both in one mx_quantize_many call: one quantize launch, one statistics
+    finalize launch)
   C = deq(A) . deq(B)^T on the block-scaled FP4 MFMA, fp32 accumulate, bf16 out
 (MXFP4 = 1x32 E2M1 blocks with E8M0 scales, floor rule, round-to-nearest-even).
 
@@ -357,11 +359,16 @@ def main():
     # events only at the boundaries of the two phases (an event between two
     # kernels costs the stream a few microseconds of its own); every call and
     # event goes to the current stream
+    # A and B go to the quantizer in one call (one shared launch, then one
+    # launch that finalizes both tensors' statistics)
+    def quantize(s, stats=True):
+        mx.mx_quantize_many(fmt, [A[s], B[s]], outs=[qa, qb], stats=[sta, stb] if stats else None,
+                            workspaces=[wsa, wsb])
+
     def step(i, ev=None):
         s = i % args.sets
         if ev: ev[0].record()
-        mx.mx_quantize(fmt, A[s], out=qa, stats=sta, workspace=wsa)
-        mx.mx_quantize(fmt, B[s], out=qb, stats=stb, workspace=wsb)
+        quantize(s)
         if ev: ev[1].record()
         mx.mx_gemm(fmt, qa, fmt, qb, c=C)
         if ev: ev[2].record()
@@ -393,21 +400,31 @@ def main():
     # scales, no statistics), the form a layer uses when fidelity is not wanted
     # (enqueued back to back like the steps, events at the boundaries)
     reps = 20
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    for i in range(reps):
-        s = i % args.sets
-        ev2[i][0].record()
-        mx.mx_quantize(fmt, A[s], out=qa, workspace=wsa)
-        mx.mx_quantize(fmt, B[s], out=qb, workspace=wsb)
-        ev2[i][1].record()
-    torch.cuda.synchronize()
-    t0s = [e[0].elapsed_time(e[1]) for e in ev2]
-    q0, q0_med = sum(t0s) / reps, statistics.median(t0s)
+
+    def timed(call):
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            ev2[i][0].record()
+            call(i % args.sets)
+            ev2[i][1].record()
+        torch.cuda.synchronize()
+        t = [e[0].elapsed_time(e[1]) for e in ev2]
+        return sum(t) / reps, statistics.median(t)
+
+    q0, q0_med = timed(lambda s: quantize(s, stats=False))
+
+    # also for information: the same quantization as two mx_quantize calls
+    # (four launches with statistics, two without)
+    def separate(s, stats=True):
+        mx.mx_quantize(fmt, A[s], out=qa, stats=sta if stats else None, workspace=wsa)
+        mx.mx_quantize(fmt, B[s], out=qb, stats=stb if stats else None, workspace=wsb)
+
+    qs, qs_med = timed(separate)
+    qs0, qs0_med = timed(lambda s: separate(s, stats=False))
     # the step left A's and B's codes of the last input set; recompute them (and
     # the product) for the fidelity figures and the parity check below
     s_last = (args.steps - 1) % args.sets
-    mx.mx_quantize(fmt, A[s_last], out=qa, stats=sta, workspace=wsa)
-    mx.mx_quantize(fmt, B[s_last], out=qb, stats=stb, workspace=wsb)
+    quantize(s_last)
     mx.mx_gemm(fmt, qa, fmt, qb, c=C)
     torch.cuda.synchronize()
 
@@ -450,18 +467,22 @@ def main():
         "quantize_codes_only": {"gbs": round(gbs(q0), 1), "frac_hbm_peak": round(gbs(q0) / HBM_PEAK_GBS, 4),
                                 "ms": round(q0, 4), "median_gbs": round(gbs(q0_med), 1),
                                 "note": "same quantizer without the fused statistics; not part of the step"},
+        "quantize_separate_calls": {"gbs": round(gbs(qs), 1), "median_gbs": round(gbs(qs_med), 1),
+                                    "codes_only_gbs": round(gbs(qs0), 1),
+                                    "codes_only_median_gbs": round(gbs(qs0_med), 1),
+                                    "note": "A and B by two mx_quantize calls instead of one "
+                                            "mx_quantize_many; not part of the step"},
         "gemm": {"tflops": round(tfs(g_ms), 1), "frac_fp4_peak": round(tfs(g_ms) / FP4_PEAK_TFLOPS, 4),
                  "ms": round(g_ms, 4), "median_ms": round(g_med, 4), "median_tflops": round(tfs(g_med), 1)},
         "roofline": {"bound": "mfma", "kernel": "block-scaled MXFP4 GEMM (k_gemm_tiled)",
                      "achieved": round(tfs(g_ms), 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs(g_ms) / FP4_PEAK_TFLOPS, 4),
                      "traffic": None if gt is None else round(gt["traffic_bytes"])},
-        "quantize_roofline": {"bound": "hbm", "kernel": "MXFP4 row quantizer with fused statistics "
-                                                        "(+ statistics finalize), A and B",
+        "quantize_roofline": {"bound": "hbm", "kernel": "MXFP4 row quantizer with fused statistics, A and B in one "
+                                                        "launch (k_rows_fast_many), + one statistics finalize",
                               "achieved": round(gbs(q_ms), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(gbs(q_ms) / HBM_PEAK_GBS, 4),
-                              "traffic": None if qt is None else round(
-                                  sum(qt[t]["fetch_bytes"] + qt[t]["write_bytes"] for t in ("A", "B")))},
+                              "traffic": None if qt is None else round(qt["fetch_bytes"] + qt["write_bytes"])},
         "qsnr_db": {"A": round(qsnr(st_a), 4), "B": round(qsnr(st_b), 4), "AB": round(qsnr_ab, 4)},
         "ceilings": ceil,
         "quantize_formats": qcells,

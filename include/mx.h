@@ -206,6 +206,39 @@ int mx_quantize_noalloc(const mx_format *f, int in_dtype, const void *x, int64_t
                         int64_t cols, int64_t ld, const mx_qtensor *out, void *dequant,
                         int dq_dtype, mx_stats *stats, void *stream);
 
+/* One tensor of an mx_quantize_many call: mx_quantize's arguments for it,
+ * without a dequantized output.  The struct and `out` are host memory; x,
+ * out's buffers, stats and workspace are device memory.  workspace: at least
+ * mx_query_sizes(f, rows, cols).workspace bytes when the job has statistics
+ * or the format a pre-pass (NULL and 0 otherwise). */
+typedef struct mx_qjob {
+    const void *x;
+    int64_t rows, cols, ld;
+    const mx_qtensor *out;
+    mx_stats *stats;
+    void *workspace;
+    size_t ws_bytes;
+} mx_qjob;
+
+/* Quantize several tensors of one format and input dtype, such as both
+ * operands of a layer's A.B^T ([U] Sec. 4, Fig. 5): job i's codes, scales and
+ * statistics are those mx_quantize(f, in_dtype, jobs[i].x, jobs[i].rows, ...)
+ * writes.  jobs: host array of `count` entries (count >= 0; jobs may be NULL
+ * when count is 0).
+ *  - Dense MXFP4-style row jobs share launches: E2M1 elements, E8M0 scales
+ *    (any rule), round to nearest, symmetric, no rotation, no macro scales,
+ *    1 x b blocks, ld == cols.  Up to eight such jobs run in one quantization launch,
+ *    their workgroups split in proportion to their sizes, and the statistics
+ *    of all of them in one finalize launch, where calling mx_quantize for
+ *    each would launch two kernels per tensor.  Every other job runs as
+ *    mx_quantize runs it, one after another.
+ *  - Every job is checked before the first launch, as mx_quantize checks its
+ *    arguments (first failing job's status); MX_ERR_ARG also when two jobs that
+ *    need a workspace name overlapping workspace bytes.
+ *  - Jobs must not write overlapping memory; the order in which they run is
+ *    unspecified.  Calls that share a workspace must not overlap. */
+int mx_quantize_many(const mx_format *f, int in_dtype, const mx_qjob *jobs, int count, void *stream);
+
 /* Dequantize q into y (rows x cols, row stride ld elements, dtype out_dtype
  * MX_DTYPE_F32 or MX_DTYPE_BF16, rounded to nearest even): each element is its
  * code's value times its block's scale (plus the block's offset when

@@ -33,7 +33,7 @@ RULE_FLOOR, RULE_CEIL, RULE_OAS = range(3)
 ROUND_RTNE, ROUND_SR, ROUND_CEIL = range(3)
 DTYPE_F32, DTYPE_BF16 = range(2)
 
-EXPORTS = ["mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_dequantize",
+EXPORTS = ["mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_quantize_many", "mx_dequantize",
            "mx_qsnr_workspace_size", "mx_qsnr", "mx_gemm", "mx_status_string"]
 
 
@@ -57,6 +57,12 @@ class MxStats(ctypes.Structure):
     _fields_ = [("sig2", ctypes.c_double), ("err2", ctypes.c_double), ("n", ctypes.c_int64),
                 ("nonzero", ctypes.c_int64), ("flushed", ctypes.c_int64),
                 ("zero_blocks", ctypes.c_int64)]
+
+
+class MxQJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld", ctypes.c_int64), ("out", ctypes.POINTER(MxQTensor)), ("stats", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
 
 
 class MxSizes(ctypes.Structure):
@@ -89,6 +95,7 @@ def lib():
         L.mx_quantize.argtypes = [P(MxFormat), i32, vp, i64, i64, i64, P(MxQTensor), vp, i32, vp,
                                   vp, ctypes.c_size_t, vp]
         L.mx_quantize_noalloc.argtypes = [P(MxFormat), i32, vp, i64, i64, i64, P(MxQTensor), vp, i32, vp, vp]
+        L.mx_quantize_many.argtypes = [P(MxFormat), i32, P(MxQJob), i32, vp]
         L.mx_dequantize.argtypes = [P(MxFormat), P(MxQTensor), i32, vp, i64, vp]
         L.mx_qsnr_workspace_size.argtypes = [i64]
         L.mx_qsnr_workspace_size.restype = ctypes.c_size_t
@@ -97,8 +104,8 @@ def lib():
         L.mx_gemm.argtypes = [P(MxFormat), P(MxQTensor), P(MxFormat), P(MxQTensor), vp, i64, i32, vp]
         L.mx_status_string.argtypes = [i32]
         L.mx_status_string.restype = ctypes.c_char_p
-        for name in ("mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_dequantize", "mx_qsnr",
-                     "mx_gemm"):
+        for name in ("mx_query_sizes", "mx_quantize", "mx_quantize_noalloc", "mx_quantize_many",
+                     "mx_dequantize", "mx_qsnr", "mx_gemm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -262,6 +269,44 @@ def mx_quantize_noalloc(fmt: Format, x: torch.Tensor, out: QTensor, dequant=None
                                    _ptr(stats), _stream(stream))
     _check(rc, "mx_quantize_noalloc")
     return out, dequant, stats
+
+
+def mx_quantize_many(fmt: Format, xs, outs=None, stats=None, workspaces=None, stream=None):
+    """Quantize several 2-D device tensors of one dtype in one format (one
+    call of mx_quantize_many).  outs: None or a list of QTensors; stats: None,
+    True (allocate one per tensor) or a list of 48-byte device tensors (or
+    None entries); workspaces: None (allocated where needed) or a list.
+    Returns (list of qtensors, list of stats tensors or None)."""
+    xs = list(xs)
+    n = len(xs)
+    outs = [None] * n if outs is None else list(outs)
+    if stats is True:
+        stats = [_empty(ctypes.sizeof(MxStats), x.device) for x in xs]
+    stats = [None] * n if stats is None else list(stats)
+    workspaces = [None] * n if workspaces is None else list(workspaces)
+    assert len(outs) == n and len(stats) == n and len(workspaces) == n
+    dt = _dtype_code(xs[0]) if n else DTYPE_BF16
+    keep = []
+    jobs = (MxQJob * max(n, 1))()
+    for i, x in enumerate(xs):
+        assert x.dim() == 2 and x.is_cuda and _dtype_code(x) == dt
+        assert x.numel() == 0 or x.stride(1) == 1
+        rows, cols = x.shape
+        if outs[i] is None:
+            outs[i] = alloc_qtensor(fmt, rows, cols, x.device)
+        if workspaces[i] is None and (stats[i] is not None or fmt.scale in (SCALE_NVFP4, SCALE_E3M0)):
+            workspaces[i] = alloc_workspace(fmt, rows, cols, x.device)
+        q = outs[i].c()
+        keep.append(q)
+        ws = workspaces[i]
+        jobs[i] = MxQJob(x.data_ptr(), rows, cols, x.stride(0) if rows > 1 and x.numel() else cols,
+                         ctypes.pointer(q),
+                         None if stats[i] is None else stats[i].data_ptr(),
+                         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
+    f = fmt.c()
+    rc = lib().mx_quantize_many(ctypes.byref(f), dt, jobs, n, _stream(stream))
+    _check(rc, "mx_quantize_many")
+    return outs, stats
 
 
 def mx_dequantize(fmt: Format, q: QTensor, out_dtype=torch.float32, y=None, stream=None):

@@ -305,6 +305,98 @@ int mx_quantize_noalloc(const mx_format* f, int in_dtype, const void* x, int64_t
                            static_cast<hipStream_t>(stream));
 }
 
+int mx_quantize_many(const mx_format* f, int in_dtype, const mx_qjob* jobs, int count, void* stream) {
+    if (count < 0 || (count > 0 && !jobs)) return MX_ERR_ARG;
+    if (count == 0) {
+        if (in_dtype != MX_DTYPE_F32 && in_dtype != MX_DTYPE_BF16) return MX_ERR_ARG;
+        return check_format(f, 0, 0);
+    }
+    // every check before the first launch
+    for (int i = 0; i < count; i++) {
+        const mx_qjob& J = jobs[i];
+        int rc = check_quantize(f, in_dtype, J.x, J.rows, J.cols, J.ld, J.out, nullptr, 0, J.stats);
+        if (rc) return rc;
+        const bool need_ws = J.stats || needs_prepass(f);
+        if (!need_ws) continue;
+        const size_t used = workspace_layout(f, J.rows, J.cols).total;
+        if (!J.workspace || J.ws_bytes < used) return MX_ERR_WORKSPACE;
+        if (!aligned16(J.workspace)) return MX_ERR_ALIGN;
+        // jobs may run at the same time: their workspaces must not overlap
+        const uintptr_t lo = (uintptr_t)J.workspace, hi = lo + used;
+        for (int k = 0; k < i; k++) {
+            const mx_qjob& O = jobs[k];
+            if (!(O.stats || needs_prepass(f))) continue;
+            const uintptr_t olo = (uintptr_t)O.workspace, ohi = olo + workspace_layout(f, O.rows, O.cols).total;
+            if (lo < ohi && olo < hi) return MX_ERR_ARG;
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int bf = in_dtype == MX_DTYPE_BF16;
+    // dense MXFP4-style rows: up to MANY_MAX jobs per launch, jobs with
+    // statistics and jobs without in separate launches (the statistics are a
+    // compile-time variant of the kernel)
+    auto shared = [&](const mx_qjob& J) {
+        if (J.rows * J.cols == 0) return false;
+        QParams p = make_params(f, bf, J.x, J.rows, J.cols, J.ld, J.out);
+        return mxk::rows_fast_ok(p);
+    };
+    for (int st = 0; st < 2; st++) {
+        mxk::FastMany m;
+        memset(&m, 0, sizeof(m));
+        int idx[mxk::MANY_MAX];
+        auto flush = [&]() -> int {
+            if (m.count == 0) return MX_OK;
+            const mx_qjob& J0 = jobs[idx[0]];
+            QParams p = make_params(f, bf, J0.x, J0.rows, J0.cols, J0.ld, J0.out);
+            p.parts = st ? m.job[0].parts : nullptr;
+            int64_t grid = 0;
+            int rc = hip_status(mxk::launch_rows_fast_many(p, m, s, &grid));
+            if (rc) return rc;
+            if (st) {
+                // each job's nb is at most its tensor's rows_fast_grid, which its
+                // workspace layout holds
+                mxk::FinalMany fm;
+                for (int k = 0; k < m.count; k++) {
+                    const mx_qjob& J = jobs[idx[k]];
+                    fm.job[k] = mxk::FinalJob{m.job[k].parts, m.job[k].nb, J.rows * J.cols, J.stats};
+                }
+                rc = hip_status(mxk::launch_stats_final_many(fm, m.count, s));
+                if (rc) return rc;
+            }
+            m.count = 0;
+            return MX_OK;
+        };
+        for (int i = 0; i < count; i++) {
+            const mx_qjob& J = jobs[i];
+            if ((J.stats != nullptr) != (st == 1) || !shared(J)) continue;
+            mxk::FastJob& F = m.job[m.count];
+            F.x = J.x;
+            F.codes = static_cast<uint8_t*>(J.out->codes);
+            F.scales = static_cast<uint8_t*>(J.out->scales);
+            F.parts = st ? reinterpret_cast<mxd::StatPart*>(static_cast<uint8_t*>(J.workspace) +
+                                                            workspace_layout(f, J.rows, J.cols).stats_off)
+                         : nullptr;
+            F.nchunks = J.rows * J.cols / (bf ? 8 : 4);
+            idx[m.count++] = i;
+            if (m.count == mxk::MANY_MAX) {
+                const int rc = flush();
+                if (rc) return rc;
+            }
+        }
+        const int rc = flush();
+        if (rc) return rc;
+    }
+    // every other job on its own
+    for (int i = 0; i < count; i++) {
+        const mx_qjob& J = jobs[i];
+        if (shared(J)) continue;
+        const int rc = launch_quantize(f, in_dtype, J.x, J.rows, J.cols, J.ld, J.out, nullptr, 0, J.stats,
+                                       static_cast<uint8_t*>(J.workspace), workspace_layout(f, J.rows, J.cols), s);
+        if (rc) return rc;
+    }
+    return MX_OK;
+}
+
 int mx_dequantize(const mx_format* f, const mx_qtensor* q, int out_dtype, void* y, int64_t ld, void* stream) {
     if (!q) return MX_ERR_ARG;
     int rc = check_format(f, q->rows, q->cols);

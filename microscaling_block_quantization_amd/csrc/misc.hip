@@ -48,8 +48,8 @@ struct StatsOut {
     long long n, nonzero, flushed, zero_blocks;
 };
 
-__global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64_t n, int64_t nelem,
-                                                    StatsOut* out) {
+// one workgroup adds n partials into *out
+__device__ __forceinline__ void stats_final(const StatPart* parts, int64_t n, int64_t nelem, StatsOut* out) {
     double s2 = 0, e2 = 0;
     unsigned long long nz = 0, fl = 0, zb = 0;
     // each thread owns the partials t, t + NT, ...; eight of them are loaded
@@ -76,6 +76,17 @@ __global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64
         o.nonzero = (long long)r.nonzero; o.flushed = (long long)r.flushed; o.zero_blocks = (long long)r.zero_blocks;
         *out = o;
     }
+}
+
+__global__ __launch_bounds__(NT) void k_stats_final(const StatPart* parts, int64_t n, int64_t nelem,
+                                                    StatsOut* out) {
+    stats_final(parts, n, nelem, out);
+}
+
+// workgroup i finalizes job i
+__global__ __launch_bounds__(NT) void k_stats_final_many(FinalMany m) {
+    const FinalJob& J = m.job[blockIdx.x];
+    stats_final(J.parts, J.n, J.nelem, static_cast<StatsOut*>(J.out));
 }
 
 __device__ __forceinline__ int read_code(const uint8_t* row, int bits, int64_t c) {
@@ -181,6 +192,12 @@ hipError_t launch_tensor_scale(const float* parts, int64_t n, int kind, float qm
 
 hipError_t launch_stats_final(const StatPart* parts, int64_t n, int64_t nelem, void* out, hipStream_t s) {
     k_stats_final<<<1, NT, 0, s>>>(parts, n, nelem, static_cast<StatsOut*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_stats_final_many(const FinalMany& m, int count, hipStream_t s) {
+    if (count < 1 || count > MANY_MAX) return hipErrorInvalidValue;
+    k_stats_final_many<<<count, NT, 0, s>>>(m);
     return hipGetLastError();
 }
 

@@ -38,6 +38,24 @@ hipError_t launch_rows(const QParams& p, bool amax_only, hipStream_t s);
 bool rows_fast_ok(const QParams& p);
 int64_t rows_fast_grid(const QParams& p);   // upper bound of the grid launch_rows_fast uses
 hipError_t launch_rows_fast(const QParams& p, hipStream_t s, int64_t* grid);
+// Several tensors of one such format and input dtype in one launch.  The
+// caller fills x, codes, scales, parts (when p.parts is set: room for nb
+// partials) and nchunks (16-byte chunks of input, nonzero) of job[0, count);
+// the launcher sets b0 and nb, the workgroups each job takes.  *grid: the
+// workgroups launched.
+constexpr int MANY_MAX = 8;
+struct FastJob {
+    const void* x;
+    uint8_t* codes;
+    uint8_t* scales;
+    mxd::StatPart* parts;
+    int64_t nchunks, b0, nb;
+};
+struct FastMany {
+    FastJob job[MANY_MAX];
+    int count;
+};
+hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid);
 // the other E2M1 round-to-nearest row formats on the hardware FP4 converter
 // (fp8 block scales, block Hadamard rotation, macro-block scales)
 bool rows_hw_ok(const QParams& p);
@@ -56,6 +74,16 @@ hipError_t launch_tensor_scale(const float* parts, int64_t n, int scale_kind, fl
 // finalize: statistics from per-workgroup partials, fixed order
 hipError_t launch_stats_final(const mxd::StatPart* parts, int64_t n, int64_t nelem, void* out,
                               hipStream_t s);
+// the same for up to MANY_MAX partial sets in one launch, one workgroup each
+struct FinalJob {
+    const mxd::StatPart* parts;
+    int64_t n, nelem;
+    void* out;
+};
+struct FinalMany {
+    FinalJob job[MANY_MAX];
+};
+hipError_t launch_stats_final_many(const FinalMany& m, int count, hipStream_t s);
 // dequantize
 hipError_t launch_dequant(const QParams& p, hipStream_t s);
 // QSNR partials between two tensors

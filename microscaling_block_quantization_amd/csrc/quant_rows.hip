@@ -543,15 +543,19 @@ constexpr int64_t FAST_MAX_GRID = 2048;
 #define FAST_WAVES 6   // waves per SIMD the register budget is sized for
 #endif
 
+// One tensor's share of a launch: workgroup blk of nblk walks the tiles of
+// x (nchunks chunks) grid-stride and writes its codes, scales and (ST) one
+// statistics partial at parts[blk].
 template <bool BF, int G, bool FLOOR, bool ST>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 : (FLOOR ? (ST ? 8 : FAST_WAVES) : FAST_WAVES - 1), 8))) void k_rows_fast(QParams p, int64_t nchunks, int lq, uint32_t fq) {
+__device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uint8_t* scales, StatPart* parts,
+                                              int64_t nchunks, int lq, uint32_t fq, int64_t blk, int64_t nblk) {
     constexpr int EPC = BF ? 8 : 4;        // elements per chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t ntiles = (nchunks + TILE_CH - 1) / TILE_CH;
-    const int64_t step = (int64_t)gridDim.x * (NT / 64);
-    const char* xin = static_cast<const char*>(p.x);
+    const int64_t step = nblk * (NT / 64);
+    const char* xin = static_cast<const char*>(x);
     // per-lane buffer offsets; the per-chunk parts are constants that go into the
     // instructions' offset fields.  A block's scale byte is stored by its first
     // lane; the others aim past the resource and the store drops them (no
@@ -576,8 +580,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
 
     auto work = [&](const u32x4* w, int64_t t) {
         const int nv = valid(t);
-        const rsrc_t rc = buf(p.codes + t * TILE_CH * CB, nv * CB);
-        const rsrc_t rs = buf(p.scales + t * (TILE_CH / G), nv / G);
+        const rsrc_t rc = buf(codes + t * TILE_CH * CB, nv * CB);
+        const rsrc_t rs = buf(scales + t * (TILE_CH / G), nv / G);
         float s2 = 0.f, e2 = 0.f;
 #pragma unroll
         for (int k = 0; k < FAST_NL; k++) {
@@ -694,14 +698,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
         // with statistics: one register tile, so that the kernel fits 64
         // registers and 8 waves per SIMD hide each other's loads (measured 3%
         // faster than the ping-pong below at 6 waves)
-        for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < ntiles; t += step) {
+        for (int64_t t = blk * (NT / 64) + wave; t < ntiles; t += step) {
             u32x4 w1[FAST_NL];
             load(w1, t);
             work(w1, t);
         }
     } else {
         // two register tiles in ping-pong: one is worked on while the other loads
-        int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave;
+        int64_t t = blk * (NT / 64) + wave;
         u32x4 wa[FAST_NL], wb[FAST_NL];
         load(wa, t);
         while (t < ntiles) {
@@ -714,8 +718,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 
             t += step;
         }
     }
-    if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, p.parts + blockIdx.x);
+    if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, parts + blk);
 }
+
+#define MX_FAST_ATTRS                                                                                        \
+    __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 : (FLOOR ? (ST ? 8 : FAST_WAVES)   \
+                                                                                 : FAST_WAVES - 1), 8)))
+
+template <bool BF, int G, bool FLOOR, bool ST>
+__global__ MX_FAST_ATTRS void k_rows_fast(QParams p, int64_t nchunks, int lq, uint32_t fq) {
+    rows_fast_run<BF, G, FLOOR, ST>(p.x, p.codes, p.scales, p.parts, nchunks, lq, fq, blockIdx.x, gridDim.x);
+}
+
+// Several tensors in one launch: tensor i takes the nb workgroups from b0 on
+// (the b0 increase with i; a workgroup finds its tensor by a scalar search).
+template <bool BF, int G, bool FLOOR, bool ST>
+__global__ MX_FAST_ATTRS void k_rows_fast_many(FastMany m, int lq, uint32_t fq) {
+    const int64_t b = blockIdx.x;
+    int i = 0;
+    for (int k = 1; k < m.count; k++)
+        if (b >= m.job[k].b0) i = k;
+    const FastJob& J = m.job[i];
+    rows_fast_run<BF, G, FLOOR, ST>(J.x, J.codes, J.scales, J.parts, J.nchunks, lq, fq, b - J.b0, J.nb);
+}
+#undef MX_FAST_ATTRS
 
 // ---------------------------------------------------------------------------
 // Wave-tile row kernel for the other dense row formats: E2M1 under UE4M3 /
@@ -1242,6 +1268,61 @@ hipError_t launch_rows_fast(const QParams& p, hipStream_t s, int64_t* grid) {
     const int g = fast_g(p);
 #define MX_FAST_CASE(BFv, Gv) \
     if (p.in_bf16 == (BFv) && g == (Gv)) return launch_fast_g<BFv, Gv>(p, s, grid);
+    MX_FAST_CASE(true, 1) MX_FAST_CASE(true, 2) MX_FAST_CASE(true, 4) MX_FAST_CASE(true, 8) MX_FAST_CASE(true, 16)
+    MX_FAST_CASE(true, 32) MX_FAST_CASE(false, 2) MX_FAST_CASE(false, 4) MX_FAST_CASE(false, 8)
+    MX_FAST_CASE(false, 16) MX_FAST_CASE(false, 32) MX_FAST_CASE(false, 64)
+#undef MX_FAST_CASE
+    return hipErrorInvalidValue;
+}
+
+namespace {
+template <bool BF, int G, bool FLOOR, bool ST>
+hipError_t launch_fast_many(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid) {
+    auto k = k_rows_fast_many<BF, G, FLOOR, ST>;
+    static int64_t cache = 0;   // one per instantiation
+    int64_t cap = resident(k, &cache);
+    if (cap > FAST_MAX_GRID) cap = FAST_MAX_GRID;
+    // the resident workgroups shared in proportion to the jobs' chunks (so the
+    // waves of every job walk about the same number of tiles), at least one
+    // and at most as many as a job's tiles fill; never more than fit at once
+    int64_t total = 0;
+    for (int i = 0; i < m.count; i++) total += m.job[i].nchunks;
+    const int64_t share = cap > m.count ? cap - m.count : 1;
+    int64_t b0 = 0;
+    for (int i = 0; i < m.count; i++) {
+        FastJob& J = m.job[i];
+        const int64_t ntiles = (J.nchunks + TILE_CH - 1) / TILE_CH;
+        const int64_t groups = (ntiles + NT / 64 - 1) / (NT / 64);
+        int64_t nb = (int64_t)((double)share * (double)J.nchunks / (double)total);
+        nb = std::min(std::max(nb, (int64_t)1), groups);
+        J.b0 = b0;
+        J.nb = nb;
+        b0 += nb;
+    }
+    *grid = b0;
+    if (b0 == 0) return hipSuccess;
+    float q = p.rule == RULE_OAS ? p.tau : 6.0f;
+    uint32_t qb;
+    memcpy(&qb, &q, 4);
+    k<<<b0, NT, 0, s>>>(m, (int)(qb >> 23) - 127, qb & 0x7fffffu);
+    return hipGetLastError();
+}
+
+template <bool BF, int G>
+hipError_t launch_fast_many_g(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid) {
+    const bool st = p.parts != nullptr;
+    if (p.rule == RULE_FLOOR)
+        return st ? launch_fast_many<BF, G, true, true>(p, m, s, grid) : launch_fast_many<BF, G, true, false>(p, m, s, grid);
+    return st ? launch_fast_many<BF, G, false, true>(p, m, s, grid) : launch_fast_many<BF, G, false, false>(p, m, s, grid);
+}
+}  // namespace
+
+hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid) {
+    *grid = 0;
+    if (m.count < 1 || m.count > MANY_MAX) return hipErrorInvalidValue;
+    const int g = fast_g(p);
+#define MX_FAST_CASE(BFv, Gv) \
+    if (p.in_bf16 == (BFv) && g == (Gv)) return launch_fast_many_g<BFv, Gv>(p, m, s, grid);
     MX_FAST_CASE(true, 1) MX_FAST_CASE(true, 2) MX_FAST_CASE(true, 4) MX_FAST_CASE(true, 8) MX_FAST_CASE(true, 16)
     MX_FAST_CASE(true, 32) MX_FAST_CASE(false, 2) MX_FAST_CASE(false, 4) MX_FAST_CASE(false, 8)
     MX_FAST_CASE(false, 16) MX_FAST_CASE(false, 32) MX_FAST_CASE(false, 64)

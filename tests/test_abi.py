@@ -41,6 +41,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(mx.MxQTensor) == 64
     assert ctypes.sizeof(mx.MxStats) == 48
     assert ctypes.sizeof(mx.MxSizes) == 56
+    assert ctypes.sizeof(mx.MxQJob) == 64
 
 
 def test_status_strings():
@@ -279,6 +280,40 @@ def test_noalloc_rejects_before_launch():
     for rows, cols, kw in ((16384, 4096, {}), (4096, 14336, dict(block_rows=8, block_cols=8)),
                            (16384, 4096, dict(scale=mx.SCALE_NVFP4, block_cols=16))):
         assert mx.mx_query_sizes(mx.Format(**kw), rows, cols)["workspace"] <= mx.NOALLOC_SCRATCH_BYTES
+
+
+def test_quantize_many_rejects_before_launch():
+    """mx_quantize_many checks every job before its first launch: a bad count
+    or job array, the first failing job's own status (even after valid jobs,
+    which would otherwise have been launched and, with no GPU, reported
+    MX_ERR_HIP), and two jobs whose workspaces overlap."""
+    L = mx.lib()
+    f = mx.MXFP4.c()
+    rows, cols = 64, 256
+    ws = mx.mx_query_sizes(mx.MXFP4, rows, cols)["workspace"]
+    qt = [mx.MxQTensor(0x100000 * (i + 1), 0x100000 * (i + 1) + 0x40000, None, None, None, None, rows, cols)
+          for i in range(3)]
+
+    def job(i, x=0x1000, stats=None, wsp=None, wsb=0, r=rows):
+        return mx.MxQJob(x, r, cols, cols, ctypes.pointer(qt[i]), stats, wsp, wsb)
+
+    def call(*jobs, count=None, dtype=mx.DTYPE_BF16):
+        arr = (mx.MxQJob * max(len(jobs), 1))(*jobs)
+        return L.mx_quantize_many(ctypes.byref(f), dtype, arr if jobs else None,
+                                  len(jobs) if count is None else count, None)
+
+    assert call(count=0) == mx.MX_OK                      # nothing to do, nothing launched
+    assert call(count=0, dtype=7) == mx.MX_ERR_ARG
+    assert call(count=-1) == mx.MX_ERR_ARG
+    assert call(count=2) == mx.MX_ERR_ARG                 # jobs NULL
+    assert call(job(0), job(1, x=None)) == mx.MX_ERR_ARG
+    assert call(job(0), job(1, x=0x1008)) == mx.MX_ERR_ALIGN
+    assert call(job(0), job(1, r=-1)) == mx.MX_ERR_ARG
+    assert call(job(0), job(1, stats=0x9000)) == mx.MX_ERR_WORKSPACE
+    assert call(job(0, stats=0x9000, wsp=0x10000, wsb=ws),
+                job(1, stats=0x9100, wsp=0x10000 + ws - 256, wsb=ws)) == mx.MX_ERR_ARG
+    assert call(job(0, stats=0x9000, wsp=0x10000, wsb=ws), job(1, stats=0x9100, wsp=0x10000, wsb=ws),
+                job(2)) == mx.MX_ERR_ARG
 
 
 def test_ceilings_library_exports_its_header():
