@@ -462,6 +462,7 @@ namespace {
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // a packed pair of bf16 as the operand of the bf16 FP4 convert.  Built by a
@@ -901,9 +902,12 @@ __device__ __forceinline__ float group_fext_g(float v, int g) {
 // MODE (power-of-two scales, FP8S false): 0 E8M0 to nearest, 1 E8M0 with
 // stochastic rounding, 2 E3M0 to nearest, 3 INT4 elements with E8M0 scales to
 // nearest (plain or min/max).  Each has its own instantiation, so that the
-// Philox state or the other modes' logic does not weigh on the rest.
-template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0>
+// Philox state or the other modes' logic does not weigh on the rest.  PLAIN:
+// no rotation and no macro scales, known at compile time, so that none of
+// their code (or its branches) is in the loop.
+template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0, bool PLAIN = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
+    const int hg = PLAIN ? 0 : h.hg, mg = PLAIN ? 0 : h.mg;
     constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
     const int lane = threadIdx.x & 63;
@@ -914,7 +918,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int lin = lane * 16, lco = lane * CB;
     const bool lead = lane % h.g == 0;
     const int lsc = lead ? lane / h.g : OOB_OFFSET;
-    const int lmc = (h.mg && lane % h.mg == 0) ? lane / h.mg : OOB_OFFSET;
+    const int lmc = (mg && lane % mg == 0) ? lane / mg : OOB_OFFSET;
     const int lof = lead ? (lane / h.g) * 2 : OOB_OFFSET;   // INT4 min/max: bf16 offset bytes
     const float gts = (FP8S && h.nvfp4 && !AMAX) ? *p.tensor_scale : 1.0f;
     const int eref = (!FP8S && !AMAX && MODE == 2) ? *p.ref_exp : 0;
@@ -926,6 +930,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     uint32_t tmax = 0;                     // AMAX: finite maximum of |x| as float bits
     double s2d = 0.0, e2d = 0.0;
     uint32_t nz = 0, fl = 0, zb = 0;
+    // fp8 block scales: per scale code c the block scale s_b, the divisor S
+    // (s_b times the NVFP4 tensor scale, rounded to fp32) and RN(1 / S), by the
+    // same arithmetic the loop would spend on them per chunk, once per workgroup
+    __shared__ f4v stab[(FP8S && !AMAX) ? 256 : 1];
+    if constexpr (FP8S && !AMAX) {
+        const int c = threadIdx.x;         // NT == 256 threads: one code each
+        const float sbc = fp8_value(h.ue5 != 0, c);
+        const float Sc = h.nvfp4 ? sbc * gts : sbc;
+        stab[c] = f4v{sbc, Sc, 1.0f / Sc, 0.f};
+        __syncthreads();
+    }
 
     auto valid = [&](int64_t t) -> int {
         const int64_t r = h.nchunks - t * TILE_CH;
@@ -936,7 +951,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         const rsrc_t rx = buf(xin + t * TILE_CH * 16, nv * 16);
         const rsrc_t rc = buf(p.codes + t * TILE_CH * CB, nv * CB);
         const rsrc_t rs = buf(p.scales + t * (TILE_CH / h.g), nv / h.g);
-        const rsrc_t rm = buf(h.mg ? p.macro + t * (TILE_CH / (h.mg ? h.mg : 1)) : p.codes, h.mg ? nv / h.mg : 0);
+        const rsrc_t rm = buf(mg ? p.macro + t * (TILE_CH / (mg ? mg : 1)) : p.codes, mg ? nv / mg : 0);
         const rsrc_t ro = buf(MODE == 3 && h.asym ? (const void*)(p.offsets + t * (TILE_CH / h.g)) : (const void*)p.codes,
                               MODE == 3 && h.asym ? (nv / h.g) * 2 : 0);
         u32x4 w[FAST_NL];
@@ -949,7 +964,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
             for (int i = 0; i < EPC; i++)
                 x[i] = BF ? ((i & 1) ? bf16hi(w[k][i >> 1]) : bf16lo(w[k][i >> 1])) : __uint_as_float(w[k][i]);
-            if (h.hg) {
+            if (hg) {
 #pragma unroll
                 for (int span = 1; span < EPC; span <<= 1) {
 #pragma unroll
@@ -960,11 +975,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                         x[i + span] = a - b;
                     }
                 }
-                if (h.hg > 1) had_stage<1>(x, lane);
-                if (h.hg > 2) had_stage<2>(x, lane);
-                if (h.hg > 4) had_stage<4>(x, lane);
-                if (h.hg > 8) had_stage<8>(x, lane);
-                if (h.hg > 16) had_stage<16>(x, lane);
+                if (hg > 1) had_stage<1>(x, lane);
+                if (hg > 2) had_stage<2>(x, lane);
+                if (hg > 4) had_stage<4>(x, lane);
+                if (hg > 8) had_stage<8>(x, lane);
+                if (hg > 16) had_stage<16>(x, lane);
 #pragma unroll
                 for (int i = 0; i < EPC; i++) x[i] = x[i] * h.hconst;
             }
@@ -980,14 +995,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
             float y[EPC];
             float sM = 1.0f;
             uint32_t smc = 0x38u;
-            if (h.mg) {
+            if (mg) {
                 uint32_t mb = 0;
 #pragma unroll
                 for (int i = 0; i < EPC; i++) {
                     const uint32_t u = __float_as_uint(x[i]) & 0x7fffffffu;
                     if (u < 0x7f800000u) mb = max(mb, u);
                 }
-                mb = group_max_g(mb, h.mg);
+                mb = group_max_g(mb, mg);
                 if (mb) {
                     const float tt = __uint_as_float(mb) / 6.0f;
                     const float mu = tt * pow2f(-flog2(tt));
@@ -1002,15 +1017,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
                     for (int i = 0; i < EPC; i++) y[i] = div_by(x[i], sM, rM);
                 }
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)smc, rm, lmc + k * (64 / h.mg), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)smc, rm, lmc + k * (64 / mg), 0, 0);
             } else {
 #pragma unroll
                 for (int i = 0; i < EPC; i++) y[i] = x[i];
             }
-            // the block maximum: float bits of |y|; NaN and Inf sort above every finite value
-            uint32_t am = 0;
+            // the block maximum: float bits of |y|; NaN and Inf sort above every finite value.
+            // bf16 in, fp8 scales, no rotation (y is x): from the 15-bit magnitudes,
+            // two per instruction, with the least nonzero magnitude minus one (zero
+            // wraps to the top) for the exact-division guard
+            const bool raw = BF && FP8S && hg == 0;
+            u32x4 m4 = w[k] & 0x7fff7fffu;
+            uint32_t am = 0, lo16 = 0xffffu;
+            if (raw) {
+                const us2 mx = __builtin_elementwise_max(__builtin_elementwise_max(as_us2(m4.x), as_us2(m4.y)),
+                                                         __builtin_elementwise_max(as_us2(m4.z), as_us2(m4.w)));
+                const us2 one = {1, 1};
+                const us2 mn = __builtin_elementwise_min(
+                    __builtin_elementwise_min(as_us2(m4.x) - one, as_us2(m4.y) - one),
+                    __builtin_elementwise_min(as_us2(m4.z) - one, as_us2(m4.w) - one));
+                am = max((uint32_t)mx[0], (uint32_t)mx[1]) << 16;
+                lo16 = min((uint32_t)mn[0], (uint32_t)mn[1]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < EPC; i++) am = max(am, __float_as_uint(y[i]) & 0x7fffffffu);
+                for (int i = 0; i < EPC; i++) am = max(am, __float_as_uint(y[i]) & 0x7fffffffu);
+            }
             am = group_max_g(am, h.g);
             const bool nonfinite = am >= 0x7f800000u;
             uint32_t cw = 0, code;
@@ -1098,7 +1129,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 }
                 if (nonfinite) cw = 0;
                 dec_fp4<EPC / 2>(cw, scale, d);
-                if (h.mg) {
+                if (mg) {
 #pragma unroll
                     for (int i = 0; i < EPC; i++) d[i] = d[i] * sM;
                 }
@@ -1109,14 +1140,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 float tt = div_lane(__uint_as_float(am), 6.0f, __uint_as_float(0x3e2aaaabu));
                 if (h.nvfp4) tt = div_lane(tt, gts, rgts);
                 const int sc = fp8_code(h.ue5 != 0, tt);
-                const float sb = fp8_value(h.ue5 != 0, sc);
-                const float S = h.nvfp4 ? sb * gts : sb;
+                const f4v te = stab[sc];
+                const float sb = te[0], S = te[1];
                 float v[EPC];
-                if (wave_needs_exact_div(y)) {
+                // a nonzero magnitude below 2^-96 (bf16 0x0f80) or a non-finite one
+                // in any lane: the exact division
+                const bool exact = raw ? __any(lo16 < 0x0f7fu || am >= 0x7f800000u) : wave_needs_exact_div(y);
+                if (exact) {
 #pragma unroll
                     for (int i = 0; i < EPC; i++) v[i] = y[i] / S;
                 } else {
-                    const float rS = 1.0f / S;
+                    const float rS = te[2];
 #pragma unroll
                     for (int i = 0; i < EPC; i++) v[i] = div_by(y[i], S, rS);
                 }
@@ -1146,12 +1180,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
             if constexpr (ST) {
                 float s2c = 0.f, e2c = 0.f;
                 uint32_t nzl = 0, zin = 0;
+                if (raw) {
+                    // x is the bf16 input: x^2 by pairs, and the zero inputs from the
+                    // magnitudes (adding 0x7fff sets bit 15 of a nonzero one)
 #pragma unroll
-                for (int i = 0; i < EPC; i++) {
-                    const float ri = x[i] - d[i];
-                    s2c = __builtin_fmaf(x[i], x[i], s2c);
-                    e2c = __builtin_fmaf(ri, ri, e2c);
-                    zin += (x[i] == 0.f) ? 1u : 0u;
+                    for (int j = 0; j < 4; j++)
+                        s2c = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w[k][j]), as_bf2(w[k][j]), s2c, false);
+                    const uint32_t g01 = __builtin_amdgcn_perm(m4.x + 0x7fff7fffu, m4.y + 0x7fff7fffu, 0x07050301u);
+                    const uint32_t g23 = __builtin_amdgcn_perm(m4.z + 0x7fff7fffu, m4.w + 0x7fff7fffu, 0x07050301u);
+                    zin = EPC - (__builtin_popcount(g01 & 0x80808080u) + __builtin_popcount(g23 & 0x80808080u));
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        const float ri = x[i] - d[i];
+                        e2c = __builtin_fmaf(ri, ri, e2c);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        const float ri = x[i] - d[i];
+                        s2c = __builtin_fmaf(x[i], x[i], s2c);
+                        e2c = __builtin_fmaf(ri, ri, e2c);
+                        zin += (x[i] == 0.f) ? 1u : 0u;
+                    }
                 }
                 nz += EPC - zin;                       // NaN counts as non-zero
                 if (codes_decide) {
@@ -1331,18 +1381,32 @@ hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, i
 }
 
 namespace {
+typedef void (*HwKernel)(QParams, HwArgs);
+
+// the instantiation for a mode, with or without rotation and macro scales
+// (E8M0 to nearest with neither takes the MXFP4 kernel, so it has no plain one)
+template <bool BF, bool FP8S, bool ST, int MODE>
+HwKernel hw_kernel(bool plain) {
+    if constexpr (FP8S || MODE != 0)
+        if (plain) return k_rows_hw<BF, FP8S, ST, false, MODE, true>;
+    return k_rows_hw<BF, FP8S, ST, false, MODE, false>;
+}
+
 template <bool BF, bool FP8S>
 hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
+    const bool plain = h.hg == 0 && h.mg == 0;
     constexpr int M1 = FP8S ? 0 : 1, M2 = FP8S ? 0 : 2, M3 = FP8S ? 0 : 3;
     const int mode = FP8S ? 0 : (h.int4 ? 3 : (h.sr ? 1 : (h.e3m0 ? 2 : 0)));
-    auto k = mode == 1 ? (st ? k_rows_hw<BF, FP8S, true, false, M1> : k_rows_hw<BF, FP8S, false, false, M1>)
-           : mode == 2 ? (st ? k_rows_hw<BF, FP8S, true, false, M2> : k_rows_hw<BF, FP8S, false, false, M2>)
-           : mode == 3 ? (st ? k_rows_hw<BF, FP8S, true, false, M3> : k_rows_hw<BF, FP8S, false, false, M3>)
-                       : (st ? k_rows_hw<BF, FP8S, true> : k_rows_hw<BF, FP8S, false>);
-    static int64_t cache[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // one per statistics and mode variant
+    const HwKernel k =
+        mode == 1   ? (st ? hw_kernel<BF, FP8S, true, M1>(plain) : hw_kernel<BF, FP8S, false, M1>(plain))
+        : mode == 2 ? (st ? hw_kernel<BF, FP8S, true, M2>(plain) : hw_kernel<BF, FP8S, false, M2>(plain))
+        : mode == 3 ? (st ? hw_kernel<BF, FP8S, true, M3>(plain) : hw_kernel<BF, FP8S, false, M3>(plain))
+                    : (st ? hw_kernel<BF, FP8S, true, 0>(plain) : hw_kernel<BF, FP8S, false, 0>(plain));
+    // one per statistics, mode and plain variant
+    static int64_t cache[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     int64_t g = fast_groups(p);
-    const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode]);
+    const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode + (plain ? 8 : 0)]);
     if (g > r) g = r;
     if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
     *grid = g;
