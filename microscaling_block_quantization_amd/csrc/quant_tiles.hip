@@ -43,7 +43,11 @@ __device__ __forceinline__ float word_elem(uint32_t w, int j) {
     else return __uint_as_float(w);
 }
 
-template <bool BF, int BR>
+// TM fixes the element kind, and with it the pass-2 route, at compile time:
+// 0 any format; 1 E2M1 with E8M0 or E3M0 scales, to nearest or stochastic
+// (the pair convert or the bit-level SR decision); 2 INT4 with E8M0 scales to
+// nearest.  The code of the other kinds and widths then drops out of the loop.
+template <bool BF, int BR, int TM>
 __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
     constexpr int CPT = BF ? 2 : 1;            // columns per thread in pass 1
     constexpr int TC = TROW / (BF ? 2 : 4);    // columns of the tile
@@ -53,7 +57,9 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
     __shared__ __attribute__((aligned(16))) uint32_t prm[TC];
     __shared__ uint32_t zmask[TC / 32];
 
-    const Elem E = make_elem(p.elem, p.asym);
+    const Elem E = make_elem(TM == 1 ? E2M1 : (TM == 2 ? INT4 : p.elem), p.asym);
+    const int scale = TM == 2 ? SC_E8M0 : p.scale;
+    const int round = TM == 2 ? RTNE : p.round;
     const int tid = threadIdx.x;
     const int64_t ctiles = (p.cols + TC - 1) / TC;
     const int64_t band = blockIdx.x / ctiles;
@@ -75,9 +81,9 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
 
     const bool two_d = p.bc > 1;
     constexpr int G1 = BR / CPT;               // lanes of one 2D block in pass 1
-    const float g = (p.scale == SC_NVFP4) ? *p.tensor_scale : 1.0f;
-    const int eref = (p.scale == SC_E3M0) ? *p.ref_exp : 0;
-    const bool ue5 = p.scale == SC_UE5M3;
+    const float g = (scale == SC_NVFP4) ? *p.tensor_scale : 1.0f;
+    const int eref = (scale == SC_E3M0) ? *p.ref_exp : 0;
+    const bool ue5 = scale == SC_UE5M3;
 
     // ---- pass 1: block maxima and scales -------------------------------------
     {
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
             kind[j] = K_POW2; e[j] = 0; sc[j] = 0; ob[j] = 0; o[j] = 0.f;
             if (!fin[j]) {
                 kind[j] = K_NAN;
-                sc[j] = (p.scale == SC_UE4M3 || p.scale == SC_NVFP4) ? 0x7f : 0xff;
+                sc[j] = (scale == SC_UE4M3 || scale == SC_NVFP4) ? 0x7f : 0xff;
             } else if (p.asym) {
                 if (E.kind == INT4) {
                     ob[j] = bf16_floor(mn[j]);
@@ -129,9 +135,9 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                     ob[j] = bf16_rne(mx[j] * 0.5f + mn[j] * 0.5f);
                     o[j] = bf16f(ob[j]);
                 }
-            } else if (p.scale == SC_E8M0) {
+            } else if (scale == SC_E8M0) {
                 e[j] = e8m0_exp(p.rule, p.tau, E, amax[j]);
-            } else if (p.scale == SC_E3M0) {
+            } else if (scale == SC_E3M0) {
                 int cdown = 7;
                 if (amax[j] > 0.f) {
                     cdown = eref - e_ceil(amax[j], E.qmax);
@@ -141,10 +147,10 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                 sc[j] = cdown;
             } else {
                 float t = amax[j] / E.qmax;
-                if (p.scale == SC_NVFP4) t = t / g;
+                if (scale == SC_NVFP4) t = t / g;
                 sc[j] = fp8_code(ue5, t);
                 const float sbv = fp8_value(ue5, sc[j]);
-                kind[j] = ((p.scale == SC_NVFP4 ? sbv * g : sbv) == 0.f) ? K_ZERO : K_DIV;
+                kind[j] = ((scale == SC_NVFP4 ? sbv * g : sbv) == 0.f) ? K_ZERO : K_DIV;
             }
         }
         if (p.asym && E.kind != INT4) {
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
         for (int j = 0; j < CPT; j++) {
             // the E8M0 code of a power-of-two scale (E3M0 keeps its step-down
             // code; pass 2 rebuilds e from it)
-            if (kind[j] == K_POW2 && p.scale != SC_E3M0) sc[j] = e[j] + 127;
+            if (kind[j] == K_POW2 && scale != SC_E3M0) sc[j] = e[j] + 127;
             prm[tid * CPT + j] = pack_prm(sc[j], kind[j], kind[j] == K_NAN ? (uint16_t)0 : ob[j]);
         }
         const int col = tid * CPT;
@@ -217,12 +223,12 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
             kd[j] = (int)((pw >> 8) & 0xff);
             of[j] = bf16f((uint16_t)(pw >> 16));
             if (kd[j] == K_POW2) {
-                const int e = p.scale == SC_E3M0 ? eref - scd[j] : scd[j] - 127;
+                const int e = scale == SC_E3M0 ? eref - scd[j] : scd[j] - 127;
                 dn[j] = pow2f(-e);
                 upv[j] = pow2f(e);
             } else {
                 const float sb = fp8_value(ue5, scd[j]);
-                dn[j] = p.scale == SC_NVFP4 ? sb * g : sb;
+                dn[j] = scale == SC_NVFP4 ? sb * g : sb;
                 upv[j] = sb;
             }
             allpow2 = allpow2 && kd[j] == K_POW2;
@@ -230,18 +236,18 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
         // E2M1 with power-of-two scales: to nearest by the pair convert on the
         // scaled values (round to nearest even, saturating, signed zero kept),
         // stochastically by sr_e2m1; then the pair decode, as the row kernels do
-        const bool hwc = E.kind == E2M1 && (p.round == RTNE || p.round == SR) && allpow2;
+        const bool hwc = E.kind == E2M1 && (round == RTNE || round == SR) && allpow2;
         // INT4 to nearest with power-of-two scales: the integer nearest |v|
         // (ties to even), capped at the largest code; the unsigned variant
         // takes a negative v as zero, the signed one keeps the sign in two's
         // complement (the general encode and decode, written out)
-        const bool i4 = E.kind == INT4 && p.round == RTNE && allpow2;
+        const bool i4 = E.kind == INT4 && round == RTNE && allpow2;
 #pragma unroll 1
         for (int row = tid >> 6; row < BR; row += NT / 64) {
             const int64_t r = r0 + row, c0 = col0 + cl;
             const u32x4 w = *reinterpret_cast<const u32x4*>(tile + row * TROW + pc * 16);
             uint32_t rnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (p.round == SR) {
+            if (round == SR) {
                 const uint64_t idx = (uint64_t)(r * p.cols + c0);
                 draws8(p.seed, p.off, idx >> 3, rnd);
                 if (!BF && (idx & 4)) {
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                 for (int j = 0; j < EPC; j++) v[j] = (p.asym ? (xs[j] - of[j]) : xs[j]) * dn[j];
                 uint32_t cw = 0;
                 f2vr dq[EPC / 2];
-                if (p.round == SR) {
+                if (round == SR) {
 #pragma unroll
                     for (int j = 0; j < EPC; j++) cw |= (uint32_t)sr_e2m1(v[j], rnd[j]) << (4 * j);
                 } else {
@@ -309,14 +315,14 @@ __global__ __launch_bounds__(NT) void k_tiles(QParams p) {
                         dv = __uint_as_float(0x7fc00000u);
                     } else if (kd[j] == K_POW2) {
                         const float v = (p.asym ? (xs[j] - of[j]) : xs[j]) * dn[j];
-                        c = encode(E, p.round, v, rnd[j]);
+                        c = encode(E, round, v, rnd[j]);
                         dv = decode(E, c) * upv[j];
                         if (p.asym) dv = dv + of[j];
                     } else {
                         const float v = kd[j] == K_ZERO ? ((fbits(xs[j]) >> 31) ? -0.f : 0.f) : xs[j] / dn[j];
-                        c = encode(E, kd[j] == K_ZERO ? RTNE : p.round, v, rnd[j]);
+                        c = encode(E, kd[j] == K_ZERO ? RTNE : round, v, rnd[j]);
                         dv = decode(E, c) * upv[j];
-                        if (p.scale == SC_NVFP4) dv = dv * g;
+                        if (scale == SC_NVFP4) dv = dv * g;
                     }
                     code[j] = c;
                     d[j] = dv;
@@ -424,10 +430,18 @@ int64_t tiles_grid(const QParams& p) {
 hipError_t launch_tiles(const QParams& p, hipStream_t s) {
     const int64_t grid = tiles_grid(p);
     if (grid == 0) return hipSuccess;
-#define MX_TILE_CASE(BFv, BRv) \
-    if (p.in_bf16 == (BFv) && p.br == (BRv)) { k_tiles<BFv, BRv><<<grid, NT, 0, s>>>(p); return hipGetLastError(); }
-    MX_TILE_CASE(true, 8) MX_TILE_CASE(true, 16) MX_TILE_CASE(true, 32)
-    MX_TILE_CASE(false, 8) MX_TILE_CASE(false, 16) MX_TILE_CASE(false, 32)
+    const int tm = (p.elem == E2M1 && (p.round == RTNE || p.round == SR) && (p.scale == SC_E8M0 || p.scale == SC_E3M0))
+                       ? 1
+                       : ((p.elem == INT4 && p.round == RTNE && p.scale == SC_E8M0) ? 2 : 0);
+#define MX_TILE_CASE(BFv, BRv, TMv)                                         \
+    if (p.in_bf16 == (BFv) && p.br == (BRv) && tm == (TMv)) {               \
+        k_tiles<BFv, BRv, TMv><<<grid, NT, 0, s>>>(p);                      \
+        return hipGetLastError();                                           \
+    }
+#define MX_TILE_TM(BFv, BRv) MX_TILE_CASE(BFv, BRv, 0) MX_TILE_CASE(BFv, BRv, 1) MX_TILE_CASE(BFv, BRv, 2)
+    MX_TILE_TM(true, 8) MX_TILE_TM(true, 16) MX_TILE_TM(true, 32)
+    MX_TILE_TM(false, 8) MX_TILE_TM(false, 16) MX_TILE_TM(false, 32)
+#undef MX_TILE_TM
 #undef MX_TILE_CASE
     return hipErrorInvalidValue;
 }
