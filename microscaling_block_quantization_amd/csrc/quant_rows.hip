@@ -442,7 +442,8 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // MXFP4 fast path: E2M1 elements, E8M0 scales (any exponent rule), round to
-// nearest even, dense rows (ld == cols).  gfx950's V_CVT_SCALEF32_PK_FP4_*
+// nearest even, dense rows (ld == cols), with or without a dense dequantized
+// output (fp32 or bf16, taken from the decode).  gfx950's V_CVT_SCALEF32_PK_FP4_*
 // rounds x * 2^-e onto E2M1 with saturation and keeps the sign of zero (two
 // elements per instruction, bf16 inputs taken directly); it reads only the
 // exponent field of its scale operand, and a zero field means 2^-127, so the
@@ -463,6 +464,7 @@ typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // a packed pair of bf16 as the operand of the bf16 FP4 convert.  Built by a
@@ -545,11 +547,13 @@ constexpr int64_t FAST_MAX_GRID = 2048;
 #endif
 
 // One tensor's share of a launch: workgroup blk of nblk walks the tiles of
-// x (nchunks chunks) grid-stride and writes its codes, scales and (ST) one
-// statistics partial at parts[blk].
-template <bool BF, int G, bool FLOOR, bool ST>
+// x (nchunks chunks) grid-stride and writes its codes, scales, (ST) one
+// statistics partial at parts[blk] and (DQ) the dequantized values to dq,
+// dense, fp32 or (dq_bf16) bf16.
+template <bool BF, int G, bool FLOOR, bool ST, bool DQ = false>
 __device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uint8_t* scales, StatPart* parts,
-                                              int64_t nchunks, int lq, uint32_t fq, int64_t blk, int64_t nblk) {
+                                              int64_t nchunks, int lq, uint32_t fq, int64_t blk, int64_t nblk,
+                                              void* dq = nullptr, int dq_bf16 = 0) {
     constexpr int EPC = BF ? 8 : 4;        // elements per chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
     const int lane = threadIdx.x & 63;
@@ -583,6 +587,10 @@ __device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uin
         const int nv = valid(t);
         const rsrc_t rc = buf(codes + t * TILE_CH * CB, nv * CB);
         const rsrc_t rs = buf(scales + t * (TILE_CH / G), nv / G);
+        // (DQ) the tile's dequantized output: EPC values of 4 or 2 bytes per chunk
+        const int dqb = dq_bf16 ? 2 : 4;
+        const rsrc_t rdq = buf(DQ ? static_cast<char*>(dq) + t * TILE_CH * EPC * dqb : static_cast<char*>(nullptr),
+                               DQ ? nv * EPC * dqb : 0);
         float s2 = 0.f, e2 = 0.f;
 #pragma unroll
         for (int k = 0; k < FAST_NL; k++) {
@@ -626,9 +634,9 @@ __device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uin
             else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)cw, rc, lco + k * 64 * CB, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(nonfinite ? 0xffu : code), rs, lsc + k * (64 / G), 0, 0);
 
-            if constexpr (ST) {
-                // dequantized values straight from the codes (value * 2^e)
-                float d[EPC];
+            // dequantized values straight from the codes (value * 2^e)
+            float d[EPC];
+            if constexpr (ST || DQ) {
                 f2v dd[EPC / 2];
                 dd[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 0);
                 dd[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, scale, 1);
@@ -638,6 +646,35 @@ __device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uin
                 }
 #pragma unroll
                 for (int j = 0; j < EPC / 2; j++) { d[2 * j] = dd[j][0]; d[2 * j + 1] = dd[j][1]; }
+            }
+            if constexpr (DQ) {
+                // a non-finite block dequantizes to NaN; bf16 keeps the upper half
+                // of each value, which is exact (E2M1 values carry 2 significant bits)
+                u32x4 o0, o1;
+                const uint32_t qn = 0x7fc00000u;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    o0[j] = nonfinite ? qn : __float_as_uint(d[j]);
+                    if constexpr (BF) o1[j] = nonfinite ? qn : __float_as_uint(d[4 + j]);
+                }
+                if (dq_bf16) {
+                    u32x4 b;
+                    b[0] = (o0[0] >> 16) | (o0[1] & 0xffff0000u);
+                    b[1] = (o0[2] >> 16) | (o0[3] & 0xffff0000u);
+                    if constexpr (BF) {
+                        b[2] = (o1[0] >> 16) | (o1[1] & 0xffff0000u);
+                        b[3] = (o1[2] >> 16) | (o1[3] & 0xffff0000u);
+                        __builtin_amdgcn_raw_buffer_store_b128(b, rdq, lane * 16 + k * 1024, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b64((u32x2){b[0], b[1]}, rdq, lane * 8 + k * 512, 0, 0);
+                    }
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(o0, rdq, lane * (EPC * 4) + k * 64 * (EPC * 4), 0, 0);
+                    if constexpr (BF)
+                        __builtin_amdgcn_raw_buffer_store_b128(o1, rdq, lane * 32 + 16 + k * 64 * 32, 0, 0);
+                }
+            }
+            if constexpr (ST) {
                 // A zero input always gets a zero code, so flushed = #zero-magnitude
                 // codes - #zero inputs (NaN and Inf count as nonzero; a non-finite
                 // block flushes nothing).  Chunks past the end read as zeros and
@@ -722,19 +759,23 @@ __device__ __forceinline__ void rows_fast_run(const void* x, uint8_t* codes, uin
     if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, parts + blk);
 }
 
-#define MX_FAST_ATTRS                                                                                        \
-    __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G >= 32 ? 4 : (FLOOR ? (ST ? 8 : FAST_WAVES)   \
-                                                                                 : FAST_WAVES - 1), 8)))
+// waves per SIMD the register budget is sized for: 8 with statistics only
+// (64 registers, so the waves cover each other's loads), fewer otherwise, and
+// 4 for statistics with a dequantized output (128 registers, no spills)
+#define MX_FAST_ATTRS(DQv)                                                                                  \
+    __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(                                               \
+        (G >= 32 || (ST && (DQv))) ? 4 : (FLOOR ? ((ST && !(DQv)) ? 8 : FAST_WAVES) : FAST_WAVES - 1), 8)))
 
-template <bool BF, int G, bool FLOOR, bool ST>
-__global__ MX_FAST_ATTRS void k_rows_fast(QParams p, int64_t nchunks, int lq, uint32_t fq) {
-    rows_fast_run<BF, G, FLOOR, ST>(p.x, p.codes, p.scales, p.parts, nchunks, lq, fq, blockIdx.x, gridDim.x);
+template <bool BF, int G, bool FLOOR, bool ST, bool DQ>
+__global__ MX_FAST_ATTRS(DQ) void k_rows_fast(QParams p, int64_t nchunks, int lq, uint32_t fq) {
+    rows_fast_run<BF, G, FLOOR, ST, DQ>(p.x, p.codes, p.scales, p.parts, nchunks, lq, fq, blockIdx.x, gridDim.x,
+                                        p.dq, p.dq_bf16);
 }
 
 // Several tensors in one launch: tensor i takes the nb workgroups from b0 on
 // (the b0 increase with i; a workgroup finds its tensor by a scalar search).
 template <bool BF, int G, bool FLOOR, bool ST>
-__global__ MX_FAST_ATTRS void k_rows_fast_many(FastMany m, int lq, uint32_t fq) {
+__global__ MX_FAST_ATTRS(false) void k_rows_fast_many(FastMany m, int lq, uint32_t fq) {
     const int64_t b = blockIdx.x;
     int i = 0;
     for (int k = 1; k < m.count; k++)
@@ -1270,9 +1311,9 @@ int64_t resident(K k, int64_t* cache) {
     return v;
 }
 
-template <bool BF, int G, bool FLOOR, bool ST>
+template <bool BF, int G, bool FLOOR, bool ST, bool DQ>
 hipError_t launch_fast(const QParams& p, hipStream_t s, int64_t* grid) {
-    auto k = k_rows_fast<BF, G, FLOOR, ST>;
+    auto k = k_rows_fast<BF, G, FLOOR, ST, DQ>;
     static int64_t cache = 0;   // one per instantiation
     int64_t g = fast_groups(p);
     const int64_t r = resident(k, &cache);
@@ -1291,12 +1332,17 @@ hipError_t launch_fast(const QParams& p, hipStream_t s, int64_t* grid) {
     return hipGetLastError();
 }
 
-template <bool BF, int G>
-hipError_t launch_fast_g(const QParams& p, hipStream_t s, int64_t* grid) {
+template <bool BF, int G, bool DQ>
+hipError_t launch_fast_d(const QParams& p, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
     if (p.rule == RULE_FLOOR)
-        return st ? launch_fast<BF, G, true, true>(p, s, grid) : launch_fast<BF, G, true, false>(p, s, grid);
-    return st ? launch_fast<BF, G, false, true>(p, s, grid) : launch_fast<BF, G, false, false>(p, s, grid);
+        return st ? launch_fast<BF, G, true, true, DQ>(p, s, grid) : launch_fast<BF, G, true, false, DQ>(p, s, grid);
+    return st ? launch_fast<BF, G, false, true, DQ>(p, s, grid) : launch_fast<BF, G, false, false, DQ>(p, s, grid);
+}
+
+template <bool BF, int G>
+hipError_t launch_fast_g(const QParams& p, hipStream_t s, int64_t* grid) {
+    return p.dq ? launch_fast_d<BF, G, true>(p, s, grid) : launch_fast_d<BF, G, false>(p, s, grid);
 }
 
 }  // namespace
@@ -1304,7 +1350,7 @@ hipError_t launch_fast_g(const QParams& p, hipStream_t s, int64_t* grid) {
 bool rows_fast_ok(const QParams& p) {
     const int g = fast_g(p);
     return p.elem == E2M1 && p.scale == SC_E8M0 && p.round == RTNE && !p.asym && !p.had && !p.macro_cols &&
-           !p.dq && p.br == 1 && p.ld == p.cols && g * (p.in_bf16 ? 8 : 4) == p.bc && g >= 1 && g <= 64 &&
+           p.br == 1 && p.ld == p.cols && g * (p.in_bf16 ? 8 : 4) == p.bc && g >= 1 && g <= 64 &&
            (g & (g - 1)) == 0 && p.cols % p.bc == 0;
 }
 

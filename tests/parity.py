@@ -24,10 +24,10 @@ def host_u8(t, n):
 
 
 def run_gpu(x, kw, dq_dtype=torch.float32, stats=True):
-    """One mx_quantize call.  dq_dtype None asks for no dequantized output:
-    MXFP4 (E2M1, E8M0 scales, RTNE, dense rows) then takes the fast kernel,
-    which is the one the benchmark times; any other output set takes the
-    general kernels."""
+    """One mx_quantize call (dq_dtype None: no dequantized output).  MXFP4
+    (E2M1, E8M0 scales, RTNE, dense rows) takes the fast kernel with every
+    output set; the benchmark times it with statistics and no dequantized
+    output.  Other formats take their own kernels."""
     xd = to_dev(x)
     q, dq, st = mx.mx_quantize(mx.Format(**kw), xd, dequant=dq_dtype, stats=True if stats else None)
     torch.cuda.synchronize()
@@ -85,9 +85,10 @@ def compare_stats(rs, st, label):
 
 def check_quantize(x, kw, label="", dq_dtype=torch.float32):
     """Full element-by-element parity of one quantization, through every
-    output set a caller can ask for: with a dequantized output and statistics
-    (the general kernels), with statistics only, and codes only (for MXFP4
-    these two take the fast kernel).  Each route is held to the oracle:
+    output set a caller can ask for: with a dequantized output and statistics,
+    with statistics only, and codes only (MXFP4 takes its fast kernel in all
+    three; the other row formats take the general row kernel when a
+    dequantized output is asked for).  Each route is held to the oracle:
     codes, scales and side outputs bit for bit, dequantized values bit for
     bit, counts exactly, QSNR within 1e-4 dB."""
     ref = oracle.quantize(x, oracle.Format(**kw),

@@ -107,7 +107,7 @@ def test_element_types(dtype, kw):
     check_dequantize(ref, q, kw, 72, 512, out_dtype=torch.bfloat16)
 
 
-# ---- the MXFP4 fast kernel (no dequantized output), every instantiation:
+# ---- the MXFP4 fast kernel (with and without a dequantized output), every instantiation:
 # bf16 and fp32 input, every block width it takes, the FLOOR rule and the
 # exact-comparison rules (CEIL, OAS); 201 x 1280 leaves a ragged last wave tile
 FAST_RULES = [dict(), dict(rule=CEIL), dict(rule=OAS, oas_tau=6.0), dict(rule=OAS, oas_tau=7.0),
