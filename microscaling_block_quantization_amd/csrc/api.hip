@@ -108,8 +108,8 @@ int64_t quant_grid(const QParams& p) {
 
 // the largest grid any call with this format and shape can launch, whatever
 // the input dtype, the dequant output and the row stride: a strided input
-// moves MXFP4 from the fast kernel (grid capped) to the general row kernel
-// (one workgroup per 256 chunks), and so does a dequant output other formats
+// moves a dense-row format from the fast or wave-tile kernel (grid capped) to
+// the general row kernel (one workgroup per 256 chunks)
 int64_t max_quant_grid(QParams p) {
     int64_t g = 0;
     for (int bf = 0; bf < 2; bf++) {

@@ -792,7 +792,7 @@ __global__ MX_FAST_ATTRS(false) void k_rows_fast_many(FastMany m, int lq, uint32
 // macro-block scaling ("Unveiling the Potential of Quantization with MXFP4",
 // Sec. 4), to nearest or (E8M0 scales) stochastically; INT4, plain or min/max,
 // under E8M0 scales to nearest (the ARITH 2025 MX-training report's
-// asymmetric INT4).  Dense rows, no dequantized output.  Wave tile, buffer
+// asymmetric INT4).  Dense rows, optional dense dequantized output.  Wave tile, buffer
 // I/O and grid-stride loop as in k_rows_fast; the lane groups (scale block: g
 // lanes, rotation chunk: hg, macro block: mg) are uniform run-time sizes.
 //  - rotation: the butterflies of a chunk's EPC elements in registers, then
@@ -945,9 +945,10 @@ __device__ __forceinline__ float group_fext_g(float v, int g) {
 // nearest (plain or min/max).  Each has its own instantiation, so that the
 // Philox state or the other modes' logic does not weigh on the rest.  PLAIN:
 // no rotation and no macro scales, known at compile time, so that none of
-// their code (or its branches) is in the loop.
-template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0, bool PLAIN = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_hw(QParams p, HwArgs h) {
+// their code (or its branches) is in the loop.  DQ: with the dense dequantized
+// output (its own instantiation, so the others keep their registers).
+template <bool BF, bool FP8S, bool ST, bool AMAX = false, int MODE = 0, bool PLAIN = false, bool DQ = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DQ ? 2 : 4, 8))) void k_rows_hw(QParams p, HwArgs h) {
     const int hg = PLAIN ? 0 : h.hg, mg = PLAIN ? 0 : h.mg;
     constexpr int EPC = BF ? 8 : 4;        // elements per 16-byte chunk
     constexpr int CB = EPC / 2;            // code bytes per chunk
@@ -1215,6 +1216,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                 for (int i = 0; i < EPC; i++)
                     if (nonfinite) d[i] = __uint_as_float(0x7fc00000u);
             }
+            if constexpr (DQ) {
+                // the dequantized values, dense: fp32, or bf16 rounded to nearest even
+                const int dqb = p.dq_bf16 ? 2 : 4;
+                const rsrc_t rdq = buf(static_cast<char*>(p.dq) + t * TILE_CH * EPC * dqb, nv * EPC * dqb);
+                if (p.dq_bf16) {
+                    uint32_t b[EPC / 2];
+#pragma unroll
+                    for (int j = 0; j < EPC / 2; j++) b[j] = bf16_rne(d[2 * j]) | ((uint32_t)bf16_rne(d[2 * j + 1]) << 16);
+                    if constexpr (BF)
+                        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b[0], b[1], b[2], b[3]}, rdq, lane * 16 + k * 1024, 0,
+                                                               0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64((u32x2){b[0], b[1]}, rdq, lane * 8 + k * 512, 0, 0);
+                } else {
+                    const u32x4 o0 = {__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
+                                      __float_as_uint(d[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(o0, rdq, lane * (EPC * 4) + k * 64 * (EPC * 4), 0, 0);
+                    if constexpr (BF) {
+                        const u32x4 o1 = {__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]),
+                                          __float_as_uint(d[7])};
+                        __builtin_amdgcn_raw_buffer_store_b128(o1, rdq, lane * 32 + 16 + k * 64 * 32, 0, 0);
+                    }
+                }
+            }
             if constexpr (BF) __builtin_amdgcn_raw_buffer_store_b32(cw, rc, lco + k * 64 * CB, 0, 0);
             else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)cw, rc, lco + k * 64 * CB, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs, lsc + k * (64 / h.g), 0, 0);
@@ -1430,29 +1455,36 @@ namespace {
 typedef void (*HwKernel)(QParams, HwArgs);
 
 // the instantiation for a mode, with or without rotation and macro scales
-// (E8M0 to nearest with neither takes the MXFP4 kernel, so it has no plain one)
-template <bool BF, bool FP8S, bool ST, int MODE>
-HwKernel hw_kernel(bool plain) {
+// (E8M0 to nearest with neither takes the MXFP4 kernel, so it has no plain
+// one), with or without the dequantized output
+template <bool BF, bool FP8S, bool ST, int MODE, bool DQ>
+HwKernel hw_kernel_d(bool plain) {
     if constexpr (FP8S || MODE != 0)
-        if (plain) return k_rows_hw<BF, FP8S, ST, false, MODE, true>;
-    return k_rows_hw<BF, FP8S, ST, false, MODE, false>;
+        if (plain) return k_rows_hw<BF, FP8S, ST, false, MODE, true, DQ>;
+    return k_rows_hw<BF, FP8S, ST, false, MODE, false, DQ>;
+}
+
+template <bool BF, bool FP8S, bool ST, int MODE>
+HwKernel hw_kernel(bool plain, bool dq) {
+    return dq ? hw_kernel_d<BF, FP8S, ST, MODE, true>(plain) : hw_kernel_d<BF, FP8S, ST, MODE, false>(plain);
 }
 
 template <bool BF, bool FP8S>
 hipError_t launch_hw_t(const QParams& p, const HwArgs& h, hipStream_t s, int64_t* grid) {
     const bool st = p.parts != nullptr;
     const bool plain = h.hg == 0 && h.mg == 0;
+    const bool dq = p.dq != nullptr;
     constexpr int M1 = FP8S ? 0 : 1, M2 = FP8S ? 0 : 2, M3 = FP8S ? 0 : 3;
     const int mode = FP8S ? 0 : (h.int4 ? 3 : (h.sr ? 1 : (h.e3m0 ? 2 : 0)));
     const HwKernel k =
-        mode == 1   ? (st ? hw_kernel<BF, FP8S, true, M1>(plain) : hw_kernel<BF, FP8S, false, M1>(plain))
-        : mode == 2 ? (st ? hw_kernel<BF, FP8S, true, M2>(plain) : hw_kernel<BF, FP8S, false, M2>(plain))
-        : mode == 3 ? (st ? hw_kernel<BF, FP8S, true, M3>(plain) : hw_kernel<BF, FP8S, false, M3>(plain))
-                    : (st ? hw_kernel<BF, FP8S, true, 0>(plain) : hw_kernel<BF, FP8S, false, 0>(plain));
-    // one per statistics, mode and plain variant
-    static int64_t cache[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        mode == 1   ? (st ? hw_kernel<BF, FP8S, true, M1>(plain, dq) : hw_kernel<BF, FP8S, false, M1>(plain, dq))
+        : mode == 2 ? (st ? hw_kernel<BF, FP8S, true, M2>(plain, dq) : hw_kernel<BF, FP8S, false, M2>(plain, dq))
+        : mode == 3 ? (st ? hw_kernel<BF, FP8S, true, M3>(plain, dq) : hw_kernel<BF, FP8S, false, M3>(plain, dq))
+                    : (st ? hw_kernel<BF, FP8S, true, 0>(plain, dq) : hw_kernel<BF, FP8S, false, 0>(plain, dq));
+    // one per statistics, mode, plain and dequant variant
+    static int64_t cache[32] = {};
     int64_t g = fast_groups(p);
-    const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode + (plain ? 8 : 0)]);
+    const int64_t r = resident(k, &cache[(st ? 1 : 0) + 2 * mode + (plain ? 8 : 0) + (dq ? 16 : 0)]);
     if (g > r) g = r;
     if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
     *grid = g;
@@ -1494,7 +1526,7 @@ bool rows_hw_ok(const QParams& p) {
     const bool round_ok = p.round == RTNE || (p.round == SR && p.scale == SC_E8M0);
     const bool elem_ok = (p.elem == E2M1 && !p.asym) ||
                          (p.elem == INT4 && p.round == RTNE && p.scale == SC_E8M0 && !p.macro_cols);
-    return elem_ok && round_ok && !p.dq && p.br == 1 && p.ld == p.cols && scale_ok &&
+    return elem_ok && round_ok && p.br == 1 && p.ld == p.cols && scale_ok &&
            g >= 1 && g <= 64 && g * epc == p.bc && (!p.had || p.had >= epc) && (!p.macro_cols || p.scale == SC_E8M0);
 }
 

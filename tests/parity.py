@@ -86,9 +86,9 @@ def compare_stats(rs, st, label):
 def check_quantize(x, kw, label="", dq_dtype=torch.float32):
     """Full element-by-element parity of one quantization, through every
     output set a caller can ask for: with a dequantized output and statistics,
-    with statistics only, and codes only (MXFP4 takes its fast kernel in all
-    three; the other row formats take the general row kernel when a
-    dequantized output is asked for).  Each route is held to the oracle:
+    with statistics only, and codes only (dense rows take the same kernel in
+    all three: the fast one for MXFP4, the wave-tile one for the formats it
+    covers).  Each route is held to the oracle:
     codes, scales and side outputs bit for bit, dequantized values bit for
     bit, counts exactly, QSNR within 1e-4 dB."""
     ref = oracle.quantize(x, oracle.Format(**kw),

@@ -124,6 +124,22 @@ def test_fast_kernel_instantiations(dtype, b, rule):
     check_quantize(x, {**rule, "block_cols": b}, f"fast {dtype} b={b} {kid(rule)}")
 
 
+# ---- bf16 dequantized output of the wave-tile row kernel's formats, both
+# input dtypes (fp32 input stores half as many bytes per chunk)
+HW_DQ_FORMATS = [dict(scale=NVFP4, block_cols=16), dict(scale=UE5M3), dict(scale=SE3M0, rule=CEIL),
+                 dict(round=SR, seed=5), dict(elem=INT4, asymmetric=1, rule=CEIL), dict(hadamard=32),
+                 dict(macro_cols=128, block_cols=16, rule=CEIL)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kw", HW_DQ_FORMATS, ids=kid)
+def test_bf16_dequant_output_wave_tile_formats(dtype, kw):
+    x = synth.w4(shape=(201, 1280), seed=61)
+    if dtype == "f32":
+        x = synth.bf16_bits_to_f32(x) * np.float32(1.0 + 2.0 ** -12)
+    check_quantize(x, kw, f"bf16 dq {dtype} {kid(kw)}", dq_dtype=torch.bfloat16)
+
+
 # ---- column and 2D blocks of every size, both dtypes
 TILE_FORMATS = [dict(), dict(round=SR, seed=3), dict(scale=NVFP4), dict(elem=INT4, asymmetric=1, rule=CEIL),
                 dict(asymmetric=1), dict(elem=E3M2), dict(scale=UE5M3, rule=CEIL), dict(scale=SE3M0, rule=CEIL),
