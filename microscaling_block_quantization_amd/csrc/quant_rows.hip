@@ -465,6 +465,7 @@ typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // a packed pair of bf16 as the operand of the bf16 FP4 convert.  Built by a
@@ -784,6 +785,162 @@ __global__ MX_FAST_ATTRS(false) void k_rows_fast_many(FastMany m, int lq, uint32
     rows_fast_run<BF, G, FLOOR, ST>(J.x, J.codes, J.scales, J.parts, J.nchunks, lq, fq, b - J.b0, J.nb);
 }
 #undef MX_FAST_ATTRS
+
+// ---------------------------------------------------------------------------
+// MXFP8 fast path: E4M3 or (E5) E5M2 elements, E8M0 scales (any exponent
+// rule), round to nearest even, dense rows; the wave tile and buffer I/O of
+// k_rows_fast, one code byte per element.  V_CVT_SCALEF32_PK_FP8_F32 /
+// _PK_BF8_F32 round x * 2^-e to nearest even but do not saturate (an overflow
+// gives the NaN / Inf code), so each element is first clamped to +-Qmax 2^e:
+// exact, and the rounding then gives Qmax for every larger magnitude, the
+// format's saturation.  The decode forms give back value * 2^e.
+// ---------------------------------------------------------------------------
+template <bool E5>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w, float a, float b, float scale, bool hi) {
+    s2v r;
+    __builtin_memcpy(&r, &w, 4);
+    r = hi ? (E5 ? __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, a, b, scale, true)
+                 : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, scale, true))
+           : (E5 ? __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, a, b, scale, false)
+                 : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, scale, false));
+    uint32_t o;
+    __builtin_memcpy(&o, &r, 4);
+    return o;
+}
+
+template <bool E5>
+__device__ __forceinline__ f2v fp8_unpair(uint32_t w, float scale, bool hi) {
+    return hi ? (E5 ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, scale, true)
+                    : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, scale, true))
+              : (E5 ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, scale, false)
+                    : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, scale, false));
+}
+
+// floor_rule and the dequantized output (p.dq) are uniform run-time switches
+template <bool BF, int G, bool ST, bool E5>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_fp8(QParams p, int64_t nchunks,
+                                                                                          int lq, uint32_t fq,
+                                                                                          int floor_rule) {
+    const bool DQ = p.dq != nullptr;
+    constexpr int EPC = BF ? 8 : 4;        // elements (and code bytes) per chunk
+    constexpr int EMAX = E5 ? 15 : 8;      // floor(log2 Qmax); Qmax = 1.75 x 2^EMAX
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (nchunks + TILE_CH - 1) / TILE_CH;
+    const int64_t step = (int64_t)gridDim.x * (NT / 64);
+    const char* xin = static_cast<const char*>(p.x);
+    const int lin = lane * 16, lco = lane * EPC;
+    const int lsc = lane % G == 0 ? lane / G : OOB_OFFSET;
+    const uint32_t lead = lane % G == 0 ? 1u : 0u;
+    double s2d = 0.0, e2d = 0.0;
+    uint32_t nz = 0, fl = 0, zb = 0;
+    for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < ntiles; t += step) {
+        const int64_t r = nchunks - t * TILE_CH;
+        const int nv = r < TILE_CH ? (int)r : TILE_CH;
+        const rsrc_t rx = buf(xin + t * TILE_CH * 16, nv * 16);
+        const rsrc_t rc = buf(p.codes + t * TILE_CH * EPC, nv * EPC);
+        const rsrc_t rs = buf(p.scales + t * (TILE_CH / G), nv / G);
+        const int dqb = p.dq_bf16 ? 2 : 4;
+        const rsrc_t rdq = buf(DQ ? static_cast<char*>(p.dq) + t * TILE_CH * EPC * dqb : static_cast<char*>(nullptr),
+                               DQ ? nv * EPC * dqb : 0);
+        u32x4 w[FAST_NL];
+#pragma unroll
+        for (int k = 0; k < FAST_NL; k++)
+            w[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lin + k * 1024, 0, CPOL_NT));
+#pragma unroll
+        for (int k = 0; k < FAST_NL; k++) {
+            float x[EPC];
+#pragma unroll
+            for (int i = 0; i < EPC; i++)
+                x[i] = BF ? ((i & 1) ? bf16hi(w[k][i >> 1]) : bf16lo(w[k][i >> 1])) : __uint_as_float(w[k][i]);
+            uint32_t am = 0;
+#pragma unroll
+            for (int i = 0; i < EPC; i++) am = max(am, __float_as_uint(x[i]) & 0x7fffffffu);
+            am = group_max_u<G>(am);
+            const bool nonfinite = am >= 0x7f800000u;
+            uint32_t sbits;
+            if (floor_rule) sbits = __builtin_elementwise_sub_sat(am & 0x7f800000u, (uint32_t)EMAX << 23);
+            else sbits = (uint32_t)(fast_exp<false>(am, lq, fq) + 127) << 23;
+            const uint32_t code = sbits >> 23;
+            const float scale = __uint_as_float(sbits);
+            // Qmax 2^e = 1.75 x 2^(e + EMAX); beyond the fp32 range no element can exceed it
+            const float c = __uint_as_float(code + EMAX >= 255 ? 0x7f800000u : ((code + EMAX) << 23) | 0x600000u);
+            uint32_t cw[EPC / 4];
+#pragma unroll
+            for (int q = 0; q < EPC / 4; q++) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) v[i] = __builtin_amdgcn_fmed3f(x[4 * q + i], -c, c);
+                uint32_t u = fp8_pair<E5>(0u, v[0], v[1], scale, false);
+                cw[q] = nonfinite ? 0u : fp8_pair<E5>(u, v[2], v[3], scale, true);
+            }
+            if constexpr (BF) __builtin_amdgcn_raw_buffer_store_b64((u32x2){cw[0], cw[1]}, rc, lco + k * 64 * EPC, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b32(cw[0], rc, lco + k * 64 * EPC, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(nonfinite ? 0xffu : code), rs, lsc + k * (64 / G), 0, 0);
+            float d[EPC];
+            if (ST || DQ) {
+#pragma unroll
+                for (int q = 0; q < EPC / 4; q++) {
+                    const f2v lo = fp8_unpair<E5>(cw[q], scale, false), hi = fp8_unpair<E5>(cw[q], scale, true);
+                    d[4 * q] = lo[0]; d[4 * q + 1] = lo[1]; d[4 * q + 2] = hi[0]; d[4 * q + 3] = hi[1];
+                }
+            }
+            if (DQ) {
+                // a non-finite block dequantizes to NaN; bf16 keeps the upper half
+                // of each value, which is exact (FP8 values carry 4 or 3 significant bits)
+                uint32_t o[EPC];
+#pragma unroll
+                for (int i = 0; i < EPC; i++) o[i] = nonfinite ? 0x7fc00000u : __float_as_uint(d[i]);
+                if (p.dq_bf16) {
+                    uint32_t b[EPC / 2];
+#pragma unroll
+                    for (int j = 0; j < EPC / 2; j++) b[j] = (o[2 * j] >> 16) | (o[2 * j + 1] & 0xffff0000u);
+                    if constexpr (BF)
+                        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b[0], b[1], b[2], b[3]}, rdq, lane * 16 + k * 1024, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64((u32x2){b[0], b[1]}, rdq, lane * 8 + k * 512, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rdq,
+                                                           lane * (EPC * 4) + k * 64 * (EPC * 4), 0, 0);
+                    if constexpr (BF)
+                        __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[4], o[5], o[6], o[7]}, rdq,
+                                                               lane * 32 + 16 + k * 64 * 32, 0, 0);
+                }
+            }
+            if constexpr (ST) {
+                // a block is all zero codes iff its (clamped) maximum rounds to a
+                // zero code; chunks past the end read as zeros and count only there
+                const float amc = __builtin_amdgcn_fmed3f(__uint_as_float(am), -c, c);
+                const uint32_t ca = fp8_pair<E5>(0u, amc, 0.f, scale, false);
+                const uint32_t allz = (!nonfinite && (ca & 0x7fu) == 0) ? 1u : 0u;
+                float s2 = 0.f, e2 = 0.f;
+#pragma unroll
+                for (int i = 0; i < EPC; i++) {
+                    const float ri = x[i] - d[i];
+                    s2 = __builtin_fmaf(x[i], x[i], s2);
+                    e2 = __builtin_fmaf(ri, ri, e2);
+                    nz += x[i] != 0.f ? 1u : 0u;
+                    fl += (!nonfinite && x[i] != 0.f && d[i] == 0.f) ? 1u : 0u;
+                }
+                zb += allz & lead & (lane + k * 64 < nv ? 1u : 0u);
+                if (nonfinite) e2 = __uint_as_float(0x7fc00000u);
+                if (fabsf(s2) < INFINITY && !nonfinite) {
+                    s2d += (double)s2;
+                    e2d += (double)e2;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < EPC; i++) {
+                        const double xd = x[i], dd = nonfinite ? (double)__uint_as_float(0x7fc00000u) : (double)d[i];
+                        s2d += xd * xd;
+                        e2d += (xd - dd) * (xd - dd);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, p.parts + blockIdx.x);
+}
 
 // ---------------------------------------------------------------------------
 // Wave-tile row kernel for the other dense row formats: E2M1 under UE4M3 /
@@ -1437,6 +1594,46 @@ hipError_t launch_fast_many_g(const QParams& p, FastMany& m, hipStream_t s, int6
     return st ? launch_fast_many<BF, G, false, true>(p, m, s, grid) : launch_fast_many<BF, G, false, false>(p, m, s, grid);
 }
 }  // namespace
+
+bool rows_fp8_ok(const QParams& p) {
+    return (p.elem == E4M3 || p.elem == E5M2) && p.scale == SC_E8M0 && p.round == RTNE && !p.asym && !p.had &&
+           !p.macro_cols && p.br == 1 && p.bc == 32 && p.ld == p.cols && p.cols % 32 == 0;
+}
+
+namespace {
+template <bool BF, bool ST, bool E5>
+hipError_t launch_fp8_t(const QParams& p, hipStream_t s, int64_t* grid) {
+    constexpr int G = BF ? 4 : 8;         // lanes per 32-element block
+    auto k = k_rows_fp8<BF, G, ST, E5>;
+    static int64_t cache = 0;   // one per instantiation
+    int64_t g = fast_groups(p);
+    const int64_t r = resident(k, &cache);
+    if (g > r) g = r;
+    if (g > FAST_MAX_GRID) g = FAST_MAX_GRID;
+    *grid = g;
+    if (g == 0) return hipSuccess;
+    // CEIL is OAS with tau = Qmax, the format's largest magnitude
+    const float q = p.rule == RULE_OAS ? p.tau : (E5 ? 57344.0f : 448.0f);
+    uint32_t qb;
+    memcpy(&qb, &q, 4);
+    const int64_t nchunks = p.rows * p.cols / (BF ? 8 : 4);
+    k<<<g, NT, 0, s>>>(p, nchunks, (int)(qb >> 23) - 127, qb & 0x7fffffu, p.rule == RULE_FLOOR ? 1 : 0);
+    return hipGetLastError();
+}
+}  // namespace
+
+int64_t rows_fp8_grid(const QParams& p) { return rows_fast_grid(p); }
+
+hipError_t launch_rows_fp8(const QParams& p, hipStream_t s, int64_t* grid) {
+    *grid = 0;
+    const bool st = p.parts != nullptr, e5 = p.elem == E5M2;
+    if (p.in_bf16) {
+        if (e5) return st ? launch_fp8_t<true, true, true>(p, s, grid) : launch_fp8_t<true, false, true>(p, s, grid);
+        return st ? launch_fp8_t<true, true, false>(p, s, grid) : launch_fp8_t<true, false, false>(p, s, grid);
+    }
+    if (e5) return st ? launch_fp8_t<false, true, true>(p, s, grid) : launch_fp8_t<false, false, true>(p, s, grid);
+    return st ? launch_fp8_t<false, true, false>(p, s, grid) : launch_fp8_t<false, false, false>(p, s, grid);
+}
 
 hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid) {
     *grid = 0;
