@@ -103,6 +103,7 @@ int64_t quant_grid(const QParams& p) {
     if (p.br > 1) return mxk::tiles_grid(p);
     if (mxk::rows_fast_ok(p)) return mxk::rows_fast_grid(p);
     if (mxk::rows_fp8_ok(p)) return mxk::rows_fp8_grid(p);
+    if (mxk::rows_fp6_ok(p)) return mxk::rows_fp6_grid(p);
     if (mxk::rows_hw_ok(p)) return mxk::rows_hw_grid(p);
     return mxk::rows_grid(p);
 }
@@ -124,6 +125,7 @@ int64_t max_quant_grid(QParams p) {
         p.ld = p.cols;
         if (mxk::rows_fast_ok(p)) g = std::max(g, mxk::rows_fast_grid(p));
         if (mxk::rows_fp8_ok(p)) g = std::max(g, mxk::rows_fp8_grid(p));
+        if (mxk::rows_fp6_ok(p)) g = std::max(g, mxk::rows_fp6_grid(p));
         if (mxk::rows_hw_ok(p)) g = std::max(g, mxk::rows_hw_grid(p));
     }
     return g;
@@ -210,6 +212,7 @@ int launch_quantize(const mx_format* f, int in_dtype, const void* x, int64_t row
         if (p.br > 1) e = mxk::launch_tiles(p, s);
         else if (mxk::rows_fast_ok(p)) e = mxk::launch_rows_fast(p, s, &grid);
         else if (mxk::rows_fp8_ok(p)) e = mxk::launch_rows_fp8(p, s, &grid);
+        else if (mxk::rows_fp6_ok(p)) e = mxk::launch_rows_fp6(p, s, &grid);
         else if (mxk::rows_hw_ok(p)) e = mxk::launch_rows_hw(p, s, &grid);
         else e = mxk::launch_rows(p, false, s);
         rc = hip_status(e);

@@ -61,6 +61,11 @@ hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, i
 bool rows_fp8_ok(const QParams& p);
 int64_t rows_fp8_grid(const QParams& p);    // upper bound of the grid launch_rows_fp8 uses
 hipError_t launch_rows_fp8(const QParams& p, hipStream_t s, int64_t* grid);
+// MXFP6 rows (E2M3 / E3M2, E8M0 scales on 1 x 32 blocks, to nearest, dense)
+// on the hardware FP6 pack converter
+bool rows_fp6_ok(const QParams& p);
+int64_t rows_fp6_grid(const QParams& p);    // upper bound of the grid launch_rows_fp6 uses
+hipError_t launch_rows_fp6(const QParams& p, hipStream_t s, int64_t* grid);
 // the other E2M1 round-to-nearest row formats on the hardware FP4 converter
 // (fp8 block scales, block Hadamard rotation, macro-block scales)
 bool rows_hw_ok(const QParams& p);

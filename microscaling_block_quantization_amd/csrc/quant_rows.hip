@@ -816,6 +816,140 @@ __device__ __forceinline__ f2v fp8_unpair(uint32_t w, float scale, bool hi) {
                     : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, scale, false));
 }
 
+// ---------------------------------------------------------------------------
+// MXFP6 fast path: E2M3 or (E3) E3M2 elements, E8M0 scales (any exponent
+// rule) on 1 x 32 blocks, round to nearest even, dense rows.  The FP6 pack
+// converts take a whole block from one lane: V_CVT_SCALEF32_PK32_FP6_BF16 /
+// _BF6_BF16 its 32 bf16 values, V_CVT_SCALEF32_2XPK16_FP6_F32 / _BF6_F32 its
+// 32 fp32 values as the even and the odd ones (element 2i from the first
+// operand, 2i + 1 from the second), and both round x * 2^-e to nearest even
+// with saturation into the 24-byte least-significant-bit-first code stream
+// of the block.  So lane l takes block l of a 64-block wave tile (64 or 128
+// contiguous bytes of input), and the decode gives the 32 values back times 2^e.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf32v __attribute__((ext_vector_type(32)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f32v __attribute__((ext_vector_type(32)));
+typedef uint32_t u6v __attribute__((ext_vector_type(6)));
+constexpr int FP6_TILE = 64 * 32;          // elements per wave tile
+
+template <bool BF, bool ST, bool E3>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_fp6(QParams p, int64_t nelem,
+                                                                                          int lq, uint32_t fq,
+                                                                                          int floor_rule) {
+    constexpr int NL = BF ? 4 : 8;         // 16-byte loads per lane (one block)
+    constexpr int EMAX = E3 ? 4 : 2;       // floor(log2 Qmax)
+    const bool DQ = p.dq != nullptr;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ntiles = (nelem + FP6_TILE - 1) / FP6_TILE;
+    const int64_t step = (int64_t)gridDim.x * (NT / 64);
+    const char* xin = static_cast<const char*>(p.x);
+    double s2d = 0.0, e2d = 0.0;
+    uint32_t nz = 0, fl = 0, zb = 0;
+    for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < ntiles; t += step) {
+        const int64_t r = nelem - t * FP6_TILE;
+        const int ne = r < FP6_TILE ? (int)r : FP6_TILE;   // a multiple of 32
+        const rsrc_t rx = buf(xin + t * FP6_TILE * (BF ? 2 : 4), ne * (BF ? 2 : 4));
+        const rsrc_t rc = buf(p.codes + t * FP6_TILE * 3 / 4, ne * 3 / 4);
+        const rsrc_t rs = buf(p.scales + t * 64, ne / 32);
+        const int dqb = p.dq_bf16 ? 2 : 4;
+        const rsrc_t rdq = buf(DQ ? static_cast<char*>(p.dq) + t * FP6_TILE * dqb : static_cast<char*>(nullptr),
+                               DQ ? ne * dqb : 0);
+        u32x4 w[NL];
+#pragma unroll
+        for (int k = 0; k < NL; k++)
+            w[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * (NL * 16) + k * 16, 0, 0));
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const uint32_t wi = w[BF ? i / 8 : i / 4][BF ? (i / 2) % 4 : i % 4];
+            x[i] = BF ? ((i & 1) ? bf16hi(wi) : bf16lo(wi)) : __uint_as_float(wi);
+        }
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < 32; i++) am = max(am, __float_as_uint(x[i]) & 0x7fffffffu);
+        const bool nonfinite = am >= 0x7f800000u;
+        uint32_t sbits;
+        if (floor_rule) sbits = __builtin_elementwise_sub_sat(am & 0x7f800000u, (uint32_t)EMAX << 23);
+        else sbits = (uint32_t)(fast_exp<false>(am, lq, fq) + 127) << 23;
+        const uint32_t code = sbits >> 23;
+        const float scale = __uint_as_float(sbits);
+        u6v cw;
+        if constexpr (BF) {
+            bf32v vb;
+            __builtin_memcpy(&vb, w, 64);
+            cw = E3 ? __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(vb, scale)
+                    : __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(vb, scale);
+        } else {
+            f16v ev, od;
+#pragma unroll
+            for (int i = 0; i < 16; i++) { ev[i] = x[2 * i]; od[i] = x[2 * i + 1]; }
+            cw = E3 ? __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, scale)
+                    : __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+        }
+        if (nonfinite) cw = (u6v){0u, 0u, 0u, 0u, 0u, 0u};
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){cw[0], cw[1], cw[2], cw[3]}, rc, lane * 24, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){cw[4], cw[5]}, rc, lane * 24 + 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(nonfinite ? 0xffu : code), rs, lane, 0, 0);
+        if (ST || DQ) {
+            const f32v dv = E3 ? __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(cw, scale)
+                               : __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(cw, scale);
+            if (DQ) {
+                // a non-finite block dequantizes to NaN; bf16 keeps the upper half of
+                // each value, which is exact (FP6 values carry 4 or 3 significant bits)
+                uint32_t o[32];
+#pragma unroll
+                for (int i = 0; i < 32; i++) o[i] = nonfinite ? 0x7fc00000u : __float_as_uint(dv[i]);
+                if (p.dq_bf16) {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        u32x4 b;
+#pragma unroll
+                        for (int j = 0; j < 4; j++) b[j] = (o[8 * q + 2 * j] >> 16) | (o[8 * q + 2 * j + 1] & 0xffff0000u);
+                        __builtin_amdgcn_raw_buffer_store_b128(b, rdq, lane * 64 + q * 16, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; q++)
+                        __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]},
+                                                               rdq, lane * 128 + q * 16, 0, 0);
+                }
+            }
+            if constexpr (ST) {
+                // lanes past the end read zeros and count only for the zero blocks
+                const bool valid = lane * 32 < ne;
+                float s2 = 0.f, e2 = 0.f;
+                uint32_t anyd = 0;
+#pragma unroll
+                for (int i = 0; i < 32; i++) {
+                    const float ri = x[i] - dv[i];
+                    s2 = __builtin_fmaf(x[i], x[i], s2);
+                    e2 = __builtin_fmaf(ri, ri, e2);
+                    nz += x[i] != 0.f ? 1u : 0u;
+                    fl += (!nonfinite && x[i] != 0.f && dv[i] == 0.f) ? 1u : 0u;
+                    anyd |= dv[i] != 0.f ? 1u : 0u;
+                }
+                zb += (valid && !nonfinite && anyd == 0) ? 1u : 0u;
+                if (fabsf(s2) < INFINITY && !nonfinite) {
+                    s2d += (double)s2;
+                    e2d += (double)e2;
+                } else {
+                    // a square beyond the fp32 range, or a NaN / Inf: this block in float64
+#pragma unroll
+                    for (int i = 0; i < 32; i++) {
+                        const double xd = x[i], dd = nonfinite ? (double)__uint_as_float(0x7fc00000u) : (double)dv[i];
+                        s2d += xd * xd;
+                        e2d += (xd - dd) * (xd - dd);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (ST) block_stats<NT>(s2d, e2d, nz, fl, zb, p.parts + blockIdx.x);
+}
+
 // floor_rule and the dequantized output (p.dq) are uniform run-time switches
 template <bool BF, int G, bool ST, bool E5>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_rows_fp8(QParams p, int64_t nchunks,
@@ -1633,6 +1767,47 @@ hipError_t launch_rows_fp8(const QParams& p, hipStream_t s, int64_t* grid) {
     }
     if (e5) return st ? launch_fp8_t<false, true, true>(p, s, grid) : launch_fp8_t<false, false, true>(p, s, grid);
     return st ? launch_fp8_t<false, true, false>(p, s, grid) : launch_fp8_t<false, false, false>(p, s, grid);
+}
+
+bool rows_fp6_ok(const QParams& p) {
+    return (p.elem == E2M3 || p.elem == E3M2) && p.scale == SC_E8M0 && p.round == RTNE && !p.asym && !p.had &&
+           !p.macro_cols && p.br == 1 && p.bc == 32 && p.ld == p.cols && p.cols % 32 == 0;
+}
+
+int64_t rows_fp6_grid(const QParams& p) {
+    const int64_t tiles = (p.rows * p.cols + FP6_TILE - 1) / FP6_TILE;
+    const int64_t g = (tiles + NT / 64 - 1) / (NT / 64);
+    return g < FAST_MAX_GRID ? g : FAST_MAX_GRID;
+}
+
+namespace {
+template <bool BF, bool ST, bool E3>
+hipError_t launch_fp6_t(const QParams& p, hipStream_t s, int64_t* grid) {
+    auto k = k_rows_fp6<BF, ST, E3>;
+    static int64_t cache = 0;   // one per instantiation
+    int64_t g = rows_fp6_grid(p);
+    const int64_t r = resident(k, &cache);
+    if (g > r) g = r;
+    *grid = g;
+    if (g == 0) return hipSuccess;
+    // CEIL is OAS with tau = Qmax, the format's largest magnitude
+    const float q = p.rule == RULE_OAS ? p.tau : (E3 ? 28.0f : 7.5f);
+    uint32_t qb;
+    memcpy(&qb, &q, 4);
+    k<<<g, NT, 0, s>>>(p, p.rows * p.cols, (int)(qb >> 23) - 127, qb & 0x7fffffu, p.rule == RULE_FLOOR ? 1 : 0);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_rows_fp6(const QParams& p, hipStream_t s, int64_t* grid) {
+    *grid = 0;
+    const bool st = p.parts != nullptr, e3 = p.elem == E3M2;
+    if (p.in_bf16) {
+        if (e3) return st ? launch_fp6_t<true, true, true>(p, s, grid) : launch_fp6_t<true, false, true>(p, s, grid);
+        return st ? launch_fp6_t<true, true, false>(p, s, grid) : launch_fp6_t<true, false, false>(p, s, grid);
+    }
+    if (e3) return st ? launch_fp6_t<false, true, true>(p, s, grid) : launch_fp6_t<false, false, true>(p, s, grid);
+    return st ? launch_fp6_t<false, true, false>(p, s, grid) : launch_fp6_t<false, false, false>(p, s, grid);
 }
 
 hipError_t launch_rows_fast_many(const QParams& p, FastMany& m, hipStream_t s, int64_t* grid) {

@@ -212,7 +212,8 @@ def test_special_values():
 
 SPECIAL_FORMATS = [dict(), dict(rule=CEIL), dict(rule=OAS, oas_tau=7.5), dict(block_cols=8),
                    dict(block_cols=64, rule=CEIL), dict(block_cols=256),
-                   dict(elem=E4M3), dict(elem=E5M2, rule=CEIL), dict(elem=E4M3, rule=OAS, oas_tau=500.0)]
+                   dict(elem=E4M3), dict(elem=E5M2, rule=CEIL), dict(elem=E4M3, rule=OAS, oas_tau=500.0),
+                   dict(elem=E2M3), dict(elem=E3M2, rule=CEIL), dict(elem=E2M3, rule=OAS, oas_tau=9.0)]
 
 
 def special_tensor_bf16():
