@@ -27,8 +27,9 @@ For information, after the timed steps (none of it is part of `value`):
                    NVFP4 / MXFP4 / UE5M3 / UE4M3 block sweep; the bf16
                    4096x14336 gradient formats over 1x32, 32x1, 32x32 blocks;
                    the bf16 16384x4096 activation formats: Hadamard, OAS, MBS,
-                   NVFP4), each timed alone after an Infinity Cache flush, with
-                   its QSNR, MSE, flush and zero-block fractions
+                   NVFP4; MXFP6 / MXFP8 operands of bf16 8192x4096), each timed
+                   alone after an Infinity Cache flush, with its QSNR, MSE,
+                   flush and zero-block fractions
   gemm_formats     the step's product in the other block formats
   parity           the step's codes, scales, statistics and 256 rows of its
                    product against the CPU oracle
@@ -238,6 +239,12 @@ def quantize_formats(mx, torch, np, synth, dev, flush):
             ("H32 -> NVFP4", F(scale=mx.SCALE_NVFP4, block_cols=16, hadamard=32))]
     for name, fmt in act:
         run("bf16 16384x4096 activation", name, fmt, x)
+    del x
+    # operands of the 6- and 8-bit products (gemm_formats): bf16 8192 x 4096 N(0, 1)
+    x = up(synth.w2(1.0))
+    for name, el in (("MXFP6 E2M3 1x32", mx.ELEM_FP6_E2M3), ("MXFP6 E3M2 1x32", mx.ELEM_FP6_E3M2),
+                     ("MXFP8 E4M3 1x32", mx.ELEM_FP8_E4M3), ("MXFP8 E5M2 1x32", mx.ELEM_FP8_E5M2)):
+        run("bf16 8192x4096 N(0,1) operand", name, F(elem=el), x)
     del x
     # the counted VALU work of the ALU-heavy cells, where it was measured
     for c in cells:
