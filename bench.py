@@ -248,7 +248,7 @@ def quantize_formats(mx, torch, np, synth, dev, flush):
     del x
     # the counted VALU work of the ALU-heavy cells, where it was measured
     for c in cells:
-        v = counted("quantize_formats_valu.json", c["format"])
+        v = counted("quantize_formats_valu.json", f"{c['format']} @ {c['config']}")
         if v is not None:
             c["alu"] = {k: v[k] for k in ("valu_insts_per_elem", "alu_bound_gbs", "note") if k in v}
     return cells

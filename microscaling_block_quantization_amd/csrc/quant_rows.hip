@@ -824,12 +824,8 @@ __device__ __forceinline__ f2v fp8_unpair(uint32_t w, float scale, bool hi) {
 // 32 fp32 values as the even and the odd ones (element 2i from the first
 // operand, 2i + 1 from the second), and both round x * 2^-e to nearest even
 // with saturation into the 24-byte least-significant-bit-first code stream
-// of the block.  So lane l takes block l of a 64-block wave tile, and the
-// decode gives the 32 values back times 2^e.  The tile is read with fully
-// coalesced 1 KiB wave loads and handed to the lanes through the wave's own
-// LDS area, each block padded by 16 bytes so that neither the writes nor the
-// reads meet a bank conflict; the wave's LDS accesses complete in order, so
-// one tile's reads are done before the next tile's writes land.
+// of the block.  So lane l takes block l of a 64-block wave tile (64 or 128
+// contiguous bytes of input), and the decode gives the 32 values back times 2^e.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf32v __attribute__((ext_vector_type(32)));
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -849,9 +845,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int64_t ntiles = (nelem + FP6_TILE - 1) / FP6_TILE;
     const int64_t step = (int64_t)gridDim.x * (NT / 64);
     const char* xin = static_cast<const char*>(p.x);
-    constexpr int BSTR = NL * 16 + 16;     // LDS bytes per block, padded
-    __shared__ __attribute__((aligned(16))) uint8_t stage[(NT / 64) * 64 * BSTR];
-    uint8_t* const ws = stage + wave * 64 * BSTR;
     double s2d = 0.0, e2d = 0.0;
     uint32_t nz = 0, fl = 0, zb = 0;
     for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < ntiles; t += step) {
@@ -866,15 +859,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         u32x4 w[NL];
 #pragma unroll
         for (int k = 0; k < NL; k++)
-            w[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16 + k * 1024, 0, CPOL_NT));
-        // chunk c = 64 k + lane belongs to block c / NL, piece c % NL
-#pragma unroll
-        for (int k = 0; k < NL; k++) {
-            const int c = 64 * k + lane;
-            *reinterpret_cast<u32x4*>(ws + (c / NL) * BSTR + (c % NL) * 16) = w[k];
-        }
-#pragma unroll
-        for (int k = 0; k < NL; k++) w[k] = *reinterpret_cast<const u32x4*>(ws + lane * BSTR + k * 16);
+            w[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * (NL * 16) + k * 16, 0, 0));
         float x[32];
 #pragma unroll
         for (int i = 0; i < 32; i++) {
