@@ -263,8 +263,12 @@ __device__ __forceinline__ void philox10(uint32_t c0, uint32_t c1, uint32_t c2, 
                                          uint32_t k0, uint32_t k1, uint32_t out[4]) {
 #pragma unroll
     for (int i = 0; i < 10; i++) {
-        uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-        uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        // each 32 x 32 -> 64-bit product as one 64-bit multiply of
+        // zero-extended operands (one v_mad_u64_u32 instead of a low and a
+        // high multiply)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
         c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
         k0 += 0x9E3779B9u;
