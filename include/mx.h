@@ -53,7 +53,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define MX_OK 0
 #define MX_ERR_ARG 1          /* bad value, shape or null pointer            */
-#define MX_ERR_UNSUPPORTED 2  /* valid format that this build does not run   */
+#define MX_ERR_UNSUPPORTED 2  /* valid format that this library does not run */
 #define MX_ERR_ALIGN 3        /* pointer or leading dimension not aligned    */
 #define MX_ERR_WORKSPACE 4    /* workspace missing or smaller than required  */
 #define MX_ERR_HIP 5          /* a HIP launch failed                         */
@@ -175,7 +175,7 @@ int mx_query_sizes(const mx_format *f, int64_t rows, int64_t cols, mx_sizes *out
  * its dequantized values, written when the stream reaches them.  workspace:
  * device scratch of at least mx_query_sizes().workspace bytes (no initial
  * contents needed); calls that share one workspace must not overlap.
- * Shapes this build runs: rows % block_rows == 0 and cols % block_cols == 0;
+ * Shapes this library runs: rows % block_rows == 0 and cols % block_cols == 0;
  * row blocks b in {8, 16, 32, 64, 128, 256} with cols % 8 == 0; column and 2D
  * blocks b in {8, 16, 32}; ld a multiple of 16 bytes.                       */
 int mx_quantize(const mx_format *f, int in_dtype, const void *x, int64_t rows,

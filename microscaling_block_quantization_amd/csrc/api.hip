@@ -258,7 +258,7 @@ const char* mx_status_string(int status) {
     switch (status) {
     case MX_OK: return "ok";
     case MX_ERR_ARG: return "invalid argument";
-    case MX_ERR_UNSUPPORTED: return "format or shape not supported by this build";
+    case MX_ERR_UNSUPPORTED: return "format or shape not supported by this library";
     case MX_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
     case MX_ERR_WORKSPACE: return "workspace missing or too small";
     case MX_ERR_HIP: return "HIP launch failed";
